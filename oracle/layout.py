@@ -15,10 +15,11 @@ Codes of a weight W [N, K] (N % 16 == 0, K % 128 == 0), KT = K / 128:
   offset (j * KT + t) * 2048: tiles of one row band are consecutive along K.
 * Inside a tile, element (r, c) (r = row within the tile, c = column within
   the tile) sits at byte  h * 1024 + lane * 16 + b  with
-  q = c // 32, h = (c % 32) // 16, b = c % 16 and lane = r + 16 * q.
-  So one wavefront lane owns 32 consecutive columns of one row (two 16-byte
-  pieces, 1024 bytes apart) and each 1024-byte half of a tile is read by one
-  64-lane, 16-bytes-per-lane load.
+  h = c // 64, q = (c % 64) // 16, b = c % 16 and lane = r + 16 * q.
+  So wavefront lane `lane` owns row lane % 16, columns 16q..16q+15 (first
+  16 bytes) and 64+16q..64+16q+15 (second 16 bytes, 1024 bytes later), which
+  is the operand order of gfx950's 16x16x128 fp8 matrix instruction; each
+  1024-byte half of a tile is read by one 64-lane, 16-bytes-per-lane load.
 
 MX scales (E8M0 bytes, logical [N, K/32]) with KG = ceil(KT / 4):
 
@@ -56,18 +57,18 @@ def pack_codes(codes):
     codes = np.asarray(codes, dtype=np.uint8)
     N, K = codes.shape
     _check(N, K)
-    # axes: j, r, t, q, h, b
-    v = codes.reshape(N // 16, 16, K // 128, 4, 2, 16)
+    # axes: j, r, t, h, q, b   (column in tile c = 64h + 16q + b)
+    v = codes.reshape(N // 16, 16, K // 128, 2, 4, 16)
     # target order: j, t, h, q, r, b  (lane = q*16 + r)
-    return np.ascontiguousarray(v.transpose(0, 2, 4, 3, 1, 5)).reshape(-1)
+    return np.ascontiguousarray(v.transpose(0, 2, 3, 4, 1, 5)).reshape(-1)
 
 
 def unpack_codes(packed, N, K):
     """Packed 1-D uint8 array -> row-major codes [N, K]."""
     _check(N, K)
     v = np.asarray(packed, dtype=np.uint8).reshape(N // 16, K // 128, 2, 4, 16, 16)
-    # axes: j, t, h, q, r, b  -> j, r, t, q, h, b
-    return np.ascontiguousarray(v.transpose(0, 4, 1, 3, 2, 5)).reshape(N, K)
+    # axes: j, t, h, q, r, b  -> j, r, t, h, q, b
+    return np.ascontiguousarray(v.transpose(0, 4, 1, 2, 3, 5)).reshape(N, K)
 
 
 def pack_mx_scales(scales):

@@ -17,24 +17,25 @@ def test_codes_roundtrip_and_size():
 
 def test_codes_hand_computed_offsets():
     # Element (n=17, k=200) of a 32x256 matrix: row band j=1, r=1; k-tile t=1,
-    # column in tile c=72 -> q=2, h=0, b=8; lane = 1 + 16*2 = 33.
-    # offset = (1*2 + 1)*2048 + 0*1024 + 33*16 + 8 = 6680.
+    # column in tile c=72 -> h=1, q=0, b=8; lane = 1 + 16*0 = 1.
+    # offset = (1*2 + 1)*2048 + 1*1024 + 1*16 + 8 = 7192.
     N, K = 32, 256
     c = np.zeros((N, K), dtype=np.uint8)
     c[17, 200] = 0xAB
     p = layout.pack_codes(c)
-    assert np.flatnonzero(p).tolist() == [6680]
-    # Element (n=0, k=31+16=47): j=0, t=0, c=47 -> q=1, h=0 (47%32=15 <16), b=15,
-    # lane 16 -> offset 16*16 + 15 = 271.  Element (n=0, k=48): c%32=16 -> h=1,
-    # b=0, lane 16 -> 1024 + 256 = 1280.
+    assert np.flatnonzero(p).tolist() == [7192]
+    # (n=0, k=47): c=47 -> h=0, q=2, b=15, lane 32 -> 32*16 + 15 = 527.
+    # (n=0, k=63): h=0, q=3, b=15, lane 48 -> 783.  (n=0, k=64): h=1, q=0,
+    # b=0, lane 0 -> 1024.
     c = np.zeros((N, K), dtype=np.uint8)
     c[0, 47] = 1
-    c[0, 48] = 2
+    c[0, 63] = 2
+    c[0, 64] = 3
     p = layout.pack_codes(c)
-    assert p[271] == 1 and p[1280] == 2 and np.count_nonzero(p) == 2
+    assert p[527] == 1 and p[783] == 2 and p[1024] == 3 and np.count_nonzero(p) == 3
 
 
-def test_each_lane_owns_32_consecutive_columns_of_one_row():
+def test_each_lane_owns_two_16_column_runs_of_one_row():
     N, K = 16, 128
     n, k = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
     ids = (n * K + k).astype(np.int64)
@@ -45,8 +46,9 @@ def test_each_lane_owns_32_consecutive_columns_of_one_row():
     for lane in range(64):
         got = np.concatenate([pid[lane * 16: lane * 16 + 16],
                               pid[1024 + lane * 16: 1024 + lane * 16 + 16]])
-        row, col0 = lane % 16, 32 * (lane // 16)
-        assert got.tolist() == [row * K + col0 + i for i in range(32)]
+        row, col0 = lane % 16, 16 * (lane // 16)
+        want = [row * K + col0 + i for i in range(16)] + [row * K + 64 + col0 + i for i in range(16)]
+        assert got.tolist() == want
 
 
 def test_mx_scales_roundtrip_padding_and_offsets():
