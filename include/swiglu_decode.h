@@ -1,0 +1,211 @@
+/*
+ * swiglu_decode.h -- C ABI of the decode-shape FP8 SwiGLU MLP library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  The layer is the SwiGLU MLP of a decoder ("activation,
+ * gate multiplication, down projection"; Fish Audio X post "We Made Our Best
+ * Voice Model Free. Here's the GPU Math Behind It.", section "Custom kernels
+ * for the shapes TTS actually uses"):
+ *
+ *     y = ( silu(x Wg^T) * (x Wu^T) ) Wd^T,   silu(g) = g / (1 + exp(-g))
+ *
+ * at decode shapes (1 <= M <= 128 rows), with FP8 E4M3 weights and
+ * activations in one of two scaling formats (same X post section; fish.audio
+ * blog "Cómo hicimos que nuestra API de texto a voz sea gratuita…", sections
+ * "Estrategia de cuantización FP8" and "Qué hay en código abierto"):
+ *
+ *   SGD_FMT_BLOCK128  one fp32 scale per 128x128 weight tile and per 1x128
+ *                     activation group; s = amax / 448, code = E4M3(v / s).
+ *   SGD_FMT_MX32      one E8M0 power-of-two scale per 1x32 block along K on
+ *                     both operands (OCP MX v1.0), 2^X with
+ *                     X = floor(log2(amax)) - 8, code = E4M3(v * 2^-X).
+ *
+ * E4M3 conversion rounds to nearest with ties to even and saturates at
+ * +-448.  The activation quantization, both GEMMs, SiLU(gate)*up and the
+ * re-quantization of that product run in ONE kernel launch
+ * (sgd_fused_swiglu_mlp); the blog's section "Resultados de benchmark del
+ * kernel" fuses activation quantization with the scale packing and the
+ * SwiGLU prologue with the down GEMM's activation quantization.
+ *
+ * Conventions shared by every call:
+ *   - Pointers to tensors are DEVICE pointers owned by the caller; bf16 is
+ *     passed as uint16_t bit patterns.  Matrices are row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; nothing synchronises the host.
+ *   - The library never allocates or frees memory and keeps no per-call
+ *     global state, so calls can be captured into a hipGraph.
+ *   - Errors detected on the host (bad argument, shape, alignment, size)
+ *     are returned as a negative sgd_status and NOTHING is launched.  A
+ *     launch failure returns SGD_EHIP.  Faults inside a kernel surface on
+ *     the caller's next stream synchronisation, as for any HIP kernel.
+ *   - Tensors whose pointer must be 16-byte aligned: bf16 x / W / y, fp8
+ *     codes, workspaces.  Scale arrays: 4-byte aligned.
+ */
+#ifndef SWIGLU_DECODE_H
+#define SWIGLU_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  SGD_OK = 0,
+  SGD_EINVAL = -1,     /* null pointer, non-positive size, M out of range   */
+  SGD_EALIGN = -2,     /* a pointer is not aligned as documented            */
+  SGD_EDIM = -3,       /* a dimension is not a multiple of its tile size    */
+  SGD_EWORKSPACE = -4, /* workspace missing or smaller than required        */
+  SGD_EFMT = -5,       /* unknown format, or operands of different formats  */
+  SGD_EHIP = -6        /* the HIP runtime refused a launch or a query       */
+};
+
+/* ---- formats ----------------------------------------------------------- */
+enum { SGD_FMT_BLOCK128 = 1, SGD_FMT_MX32 = 2 };
+
+#define SGD_MAX_M 128 /* largest row count of sgd_scaled_gemm / fused MLP */
+
+/*
+ * A packed (pre-shuffled) FP8 weight W [N, K] in nn.Linear orientation
+ * (y = x W^T).  `codes` and `scales` are device buffers of
+ * sgd_packed_codes_bytes / sgd_packed_scales_bytes bytes written by
+ * sgd_quantize_pack_weight.  N and K are multiples of 128.
+ *
+ * Packed code layout: 16x128 tiles, tile (j, t) at byte (j*(K/128) + t)*2048;
+ * element (r, c) of a tile at byte h*1024 + lane*16 + b with h = c/64,
+ * q = (c%64)/16, b = c%16, lane = r + 16*q (the operand order of the
+ * 16x16x128 fp8 MFMA: lane l owns row l%16).
+ * Scales: BLOCK128 -> fp32 [N/128, K/128] row-major.  MX32 -> E8M0 bytes;
+ * for row band j and k-tile group g (4 k-tiles) 256 bytes at
+ * (j*ceil(K/512) + g)*256, byte lane*4 + i = scale of row 16j + lane%16,
+ * 32-column block 4*(4g+i) + lane/16; bytes past K are zero.
+ */
+typedef struct sgd_weight {
+  int32_t fmt;        /* SGD_FMT_BLOCK128 or SGD_FMT_MX32 */
+  int32_t N;          /* output features (rows of W)       */
+  int32_t K;          /* input features (columns of W)     */
+  int32_t reserved;   /* must be 0                         */
+  const void* codes;  /* packed E4M3 codes, device          */
+  const void* scales; /* packed scales, device              */
+} sgd_weight;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sgd_status_str(int status);
+
+/* ABI version of this header (bumped on incompatible change). */
+int sgd_abi_version(void);
+
+/* ---- sizes ------------------------------------------------------------- */
+/* Bytes of the packed codes / packed scales of an N x K weight; 0 if the
+ * format or a dimension is invalid (N, K must be positive multiples of 128). */
+size_t sgd_packed_codes_bytes(int fmt, int N, int K);
+size_t sgd_packed_scales_bytes(int fmt, int N, int K);
+
+/*
+ * Quantize a bf16 weight W [N, K] (row-major) and write it in the packed
+ * layout.  One launch.  BLOCK128: amax over each 128x128 tile, s = amax/448
+ * (IEEE fp32 division; s = 1 for an all-zero tile), codes E4M3(w / s).
+ * MX32: per row, per 32 columns, E8M0 X = floor(log2 amax) - 8 (E = 0 for
+ * an all-zero block), codes E4M3(w * 2^-X).  Passage: fish.audio blog,
+ * section "Estrategia de cuantización FP8" (128x128 block and 1x32 UE8M0
+ * microscaling) and the X post section "Custom kernels for the shapes TTS
+ * actually uses".  The output is bit-identical to the plain definition.
+ * Errors: SGD_EFMT, SGD_EINVAL (null, N/K <= 0), SGD_EDIM (N or K not a
+ * multiple of 128), SGD_EALIGN.
+ */
+int sgd_quantize_pack_weight(int fmt, const uint16_t* w_bf16, int N, int K,
+                             void* codes_out, void* scales_out, void* stream);
+
+/*
+ * Inverse of the packing (for inspection and tests): codes_rowmajor [N, K]
+ * uint8 and scales in logical layout (BLOCK128 fp32 [N/128, K/128];
+ * MX32 uint8 [N, K/32]).  Errors as sgd_quantize_pack_weight.
+ */
+int sgd_unpack_weight(const sgd_weight* w, uint8_t* codes_rowmajor,
+                      void* scales_logical, void* stream);
+
+/*
+ * Per-row activation quantization of x [M, K] bf16 along K: BLOCK128 groups
+ * of 128 (fp32 scales [M, K/128]) or MX32 blocks of 32 (E8M0 [M, K/32]),
+ * same rules as the weights.  This is the prologue the fused kernels run
+ * internally (fish.audio blog, section "Resultados de benchmark del kernel":
+ * activation quantization and UE8M0 scale packing in one launch).
+ * 1 <= M <= 65536; K a positive multiple of 128.
+ */
+int sgd_quantize_act(int fmt, const uint16_t* x_bf16, int M, int K,
+                     uint8_t* codes, void* scales, void* stream);
+
+/* ---- workspaces -------------------------------------------------------- */
+/*
+ * The GEMM and MLP kernels need a device workspace for the quantized
+ * activations, the SwiGLU intermediate, split-K partial sums and
+ * synchronisation counters.  It must be zero-filled ONCE after allocation
+ * (sgd_workspace_clear or any fill kernel); every call leaves the counters
+ * zero again on exit.  Calls that share a workspace must not overlap
+ * (serialise them on one stream).  Size in bytes; 0 on invalid arguments.
+ */
+size_t sgd_gemm_workspace_bytes(int fmt, int M, int N, int K);
+size_t sgd_mlp_workspace_bytes(int fmt, int M, int d, int ffn);
+
+/* Zero-fill `bytes` bytes of `workspace` with a fill kernel (no memset
+ * node, so it is safe to capture).  bytes must be a multiple of 16. */
+int sgd_workspace_clear(void* workspace, size_t bytes, void* stream);
+
+/* ---- the hot path ------------------------------------------------------ */
+/*
+ * y [M, N] bf16 = Q(x) * W^T: x [M, K] bf16 is quantized per row in W's
+ * format, multiplied by the packed weight with fp32 accumulation on the
+ * MFMA units, and rounded to bf16 (nearest-even).  One launch.  Passage:
+ * fish.audio blog, section "Qué hay en código abierto" (FP8 GEMM with 1x128
+ * activation x 128x128 weight blocks, and MXFP8 1x32 UE8M0).
+ * 1 <= M <= SGD_MAX_M.  Errors: SGD_EINVAL, SGD_EALIGN, SGD_EDIM, SGD_EFMT,
+ * SGD_EWORKSPACE (ws_bytes < sgd_gemm_workspace_bytes).
+ */
+int sgd_scaled_gemm(const uint16_t* x_bf16, int M, const sgd_weight* w,
+                    uint16_t* y_bf16, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * y [M, d] bf16 = SwiGLU MLP of x [M, d] bf16 with packed gate [ffn, d],
+ * up [ffn, d] and down [d, ffn] weights, all in one format.  ONE launch:
+ * quantize x; g = Q(x) Wg^T and u = Q(x) Wu^T in fp32; a = silu(g) * u in
+ * fp32; re-quantize a per row along ffn in the same format; y = Q(a) Wd^T
+ * in fp32; round to bf16.  The intermediates stay in the workspace (on-chip
+ * caches in practice) and never round-trip through a separate launch.
+ * 1 <= M <= SGD_MAX_M; d and ffn multiples of 128.  Errors as
+ * sgd_scaled_gemm, plus SGD_EFMT when the three weights differ in format
+ * and SGD_EDIM when their shapes do not chain.
+ */
+int sgd_fused_swiglu_mlp(const uint16_t* x_bf16, int M, const sgd_weight* gate,
+                         const sgd_weight* up, const sgd_weight* down,
+                         uint16_t* y_bf16, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/* ---- decode-stack glue (pre-RMSNorm residual blocks + output head) ----- */
+/* h [M, d] fp32 <- x [M, d] bf16 (exact widening).  d multiple of 128. */
+int sgd_bf16_to_f32(const uint16_t* x_bf16, int M, int d, float* h, void* stream);
+
+/* x [M, d] bf16 = bf16( h / sqrt(mean(h^2) + eps) ) per row, unit gain
+ * (Zhang & Sennrich 2019, RMSNorm).  d multiple of 128. */
+int sgd_rmsnorm_bf16(const float* h, int M, int d, float eps, uint16_t* x_bf16,
+                     void* stream);
+
+/* h [M, d] fp32 += y [M, d] bf16 (the residual add). */
+int sgd_residual_add(float* h, const uint16_t* y_bf16, int M, int d, void* stream);
+
+/* logits [M, N] fp32 = bf16(h) [M, K] * W^T with W [N, K] bf16 row-major,
+ * fp32 accumulation (the bf16 output head).  h is fp32 and is rounded to
+ * bf16 (nearest-even) on load.  M <= 128, N and K multiples of 128. */
+int sgd_head_logits(const float* h, int M, int K, const uint16_t* w_bf16, int N,
+                    float* logits, void* stream);
+
+/* out[m] = argmax_n logits[m, n] (lowest index among equal maxima). */
+int sgd_argmax_rows(const float* logits, int M, int N, int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_DECODE_H */

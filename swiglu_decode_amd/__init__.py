@@ -1,0 +1,260 @@
+"""MI355X (gfx950) decode-shape FP8 SwiGLU MLP: Python binding.
+
+Thin wrappers over the C ABI in include/swiglu_decode.h.  PyTorch only
+supplies device memory and the current stream; every step of the path runs
+in the library's HIP kernels.  Arguments are checked (dtype, exact shape,
+contiguity, device) and never coerced: a wrong tensor raises instead of being
+converted.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import FMT_BLOCK128, FMT_MX32, MAX_M, SgdError, SgdWeight
+
+__all__ = [
+    "FMT_BLOCK128", "FMT_MX32", "MAX_M", "SgdError", "PackedWeight", "Workspace",
+    "fmt_code", "quantize_pack_weight", "unpack_weight", "quantize_act", "scaled_gemm",
+    "fused_swiglu_mlp", "bf16_to_f32", "rmsnorm_bf16", "residual_add", "head_logits",
+    "argmax_rows", "gemm_workspace_bytes", "mlp_workspace_bytes", "lib",
+]
+
+_FMTS = {"block": FMT_BLOCK128, "mx": FMT_MX32, FMT_BLOCK128: FMT_BLOCK128, FMT_MX32: FMT_MX32}
+
+
+def lib():
+    return _lib.load()
+
+
+def fmt_code(fmt):
+    if fmt not in _FMTS:
+        raise ValueError(f"unknown format {fmt!r} (use 'block' or 'mx')")
+    return _FMTS[fmt]
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+@dataclass
+class PackedWeight:
+    """A weight [N, K] quantized and packed by quantize_pack_weight."""
+    fmt: int
+    N: int
+    K: int
+    codes: torch.Tensor   # uint8 [packed_codes_bytes]
+    scales: torch.Tensor  # uint8 [packed_scales_bytes] (fp32 for block format)
+
+    def c_struct(self):
+        return SgdWeight(self.fmt, self.N, self.K, 0, self.codes.data_ptr(), self.scales.data_ptr())
+
+    @property
+    def device(self):
+        return self.codes.device
+
+
+def quantize_pack_weight(w, fmt):
+    """bf16 weight [N, K] on the GPU -> PackedWeight (one launch)."""
+    f = fmt_code(fmt)
+    if w.dim() != 2:
+        raise ValueError("weight must be 2-D [N, K]")
+    _need(w, "w", torch.bfloat16)
+    N, K = w.shape
+    L = lib()
+    nc = L.sgd_packed_codes_bytes(f, N, K)
+    ns = L.sgd_packed_scales_bytes(f, N, K)
+    if nc == 0 or ns == 0:
+        raise ValueError(f"invalid weight shape {N}x{K} for the packed layout (multiples of 128)")
+    codes = torch.empty(nc, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(ns, dtype=torch.uint8, device=w.device)
+    _lib.check("sgd_quantize_pack_weight",
+               L.sgd_quantize_pack_weight(f, _ptr(w), N, K, _ptr(codes), _ptr(scales), _stream(w)))
+    return PackedWeight(f, N, K, codes, scales)
+
+
+def unpack_weight(pw):
+    """PackedWeight -> (codes uint8 [N, K], scales logical: fp32 [N/128, K/128] or uint8 [N, K/32])."""
+    codes = torch.empty((pw.N, pw.K), dtype=torch.uint8, device=pw.device)
+    if pw.fmt == FMT_BLOCK128:
+        scales = torch.empty((pw.N // 128, pw.K // 128), dtype=torch.float32, device=pw.device)
+    else:
+        scales = torch.empty((pw.N, pw.K // 32), dtype=torch.uint8, device=pw.device)
+    st = pw.c_struct()
+    _lib.check("sgd_unpack_weight",
+               lib().sgd_unpack_weight(ctypes.byref(st), _ptr(codes), _ptr(scales), _stream(codes)))
+    return codes, scales
+
+
+def quantize_act(x, fmt):
+    """bf16 x [M, K] -> (codes uint8 [M, K], scales fp32 [M, K/128] | uint8 [M, K/32])."""
+    f = fmt_code(fmt)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    _need(x, "x", torch.bfloat16)
+    M, K = x.shape
+    codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if f == FMT_BLOCK128:
+        scales = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    else:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _lib.check("sgd_quantize_act",
+               lib().sgd_quantize_act(f, _ptr(x), M, K, _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def gemm_workspace_bytes(fmt, M, N, K):
+    return lib().sgd_gemm_workspace_bytes(fmt_code(fmt), M, N, K)
+
+
+def mlp_workspace_bytes(fmt, M, d, ffn):
+    return lib().sgd_mlp_workspace_bytes(fmt_code(fmt), M, d, ffn)
+
+
+class Workspace:
+    """A zero-initialised device workspace that grows on demand.  The kernels
+    leave its control block zeroed after every call; calls sharing one
+    workspace must be serialised on one stream."""
+
+    def __init__(self, device, nbytes=0):
+        self.device = torch.device(device)
+        self.tensor = None
+        if nbytes:
+            self.ensure(nbytes)
+
+    def ensure(self, nbytes):
+        nbytes = (int(nbytes) + 255) // 256 * 256
+        if self.tensor is None or self.tensor.numel() < nbytes:
+            self.tensor = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            _lib.check("sgd_workspace_clear",
+                       lib().sgd_workspace_clear(_ptr(self.tensor), nbytes, _stream(self.tensor)))
+        return self.tensor
+
+
+_DEFAULT_WS = {}
+
+
+def _workspace(device, nbytes, ws):
+    if ws is None:
+        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+        ws = _DEFAULT_WS.get(key)
+        if ws is None:
+            ws = _DEFAULT_WS[key] = Workspace(device)
+    t = ws.ensure(nbytes)
+    return t
+
+
+def scaled_gemm(x, w, out=None, workspace=None):
+    """y [M, N] bf16 = Q(x) W^T for bf16 x [M, K] and a PackedWeight [N, K]."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    _need(x, "x", torch.bfloat16, device=w.device)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, weight has K={w.K}")
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (M, w.N), x.device)
+    need = lib().sgd_gemm_workspace_bytes(w.fmt, M, w.N, w.K)
+    if need == 0:
+        raise ValueError(f"unsupported GEMM shape M={M} N={w.N} K={w.K}")
+    ws = _workspace(x.device, need, workspace)
+    st = w.c_struct()
+    _lib.check("sgd_scaled_gemm", lib().sgd_scaled_gemm(
+        _ptr(x), M, ctypes.byref(st), _ptr(out), _ptr(ws), ws.numel(), _stream(x)))
+    return out
+
+
+def fused_swiglu_mlp(x, gate, up, down, out=None, workspace=None):
+    """y [M, d] bf16 = SwiGLU MLP of bf16 x [M, d] (one launch)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, d]")
+    _need(x, "x", torch.bfloat16, device=gate.device)
+    M, d = x.shape
+    if gate.K != d:
+        raise ValueError(f"x has d={d}, gate weight has K={gate.K}")
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (M, d), x.device)
+    need = lib().sgd_mlp_workspace_bytes(gate.fmt, M, d, gate.N)
+    if need == 0:
+        raise ValueError(f"unsupported MLP shape M={M} d={d} ffn={gate.N}")
+    ws = _workspace(x.device, need, workspace)
+    g, u, dn = gate.c_struct(), up.c_struct(), down.c_struct()
+    _lib.check("sgd_fused_swiglu_mlp", lib().sgd_fused_swiglu_mlp(
+        _ptr(x), M, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), _ptr(out),
+        _ptr(ws), ws.numel(), _stream(x)))
+    return out
+
+
+def bf16_to_f32(x, out=None):
+    _need(x, "x", torch.bfloat16)
+    M, d = x.shape
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (M, d), x.device)
+    _lib.check("sgd_bf16_to_f32", lib().sgd_bf16_to_f32(_ptr(x), M, d, _ptr(out), _stream(x)))
+    return out
+
+
+def rmsnorm_bf16(h, eps=1e-6, out=None):
+    _need(h, "h", torch.float32)
+    M, d = h.shape
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=h.device)
+    _need(out, "out", torch.bfloat16, (M, d), h.device)
+    _lib.check("sgd_rmsnorm_bf16", lib().sgd_rmsnorm_bf16(_ptr(h), M, d, float(eps), _ptr(out), _stream(h)))
+    return out
+
+
+def residual_add(h, y):
+    _need(h, "h", torch.float32)
+    _need(y, "y", torch.bfloat16, tuple(h.shape), h.device)
+    M, d = h.shape
+    _lib.check("sgd_residual_add", lib().sgd_residual_add(_ptr(h), _ptr(y), M, d, _stream(h)))
+    return h
+
+
+def head_logits(h, w, out=None):
+    _need(h, "h", torch.float32)
+    M, K = h.shape
+    _need(w, "w", torch.bfloat16, device=h.device)
+    N = w.shape[0]
+    if tuple(w.shape) != (N, K):
+        raise ValueError(f"head weight must be [N, {K}], got {tuple(w.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=h.device)
+    _need(out, "out", torch.float32, (M, N), h.device)
+    _lib.check("sgd_head_logits", lib().sgd_head_logits(_ptr(h), M, K, _ptr(w), N, _ptr(out), _stream(h)))
+    return out
+
+
+def argmax_rows(logits, out=None):
+    _need(logits, "logits", torch.float32)
+    M, N = logits.shape
+    if out is None:
+        out = torch.empty((M,), dtype=torch.int32, device=logits.device)
+    _need(out, "out", torch.int32, (M,), logits.device)
+    _lib.check("sgd_argmax_rows", lib().sgd_argmax_rows(_ptr(logits), M, N, _ptr(out), _stream(logits)))
+    return out

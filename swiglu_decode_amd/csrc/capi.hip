@@ -1,0 +1,197 @@
+// C ABI entry points: host-side validation, then one launch on the caller's
+// stream.  Nothing is launched when validation fails.
+#include "sgd_host.hpp"
+
+#include <stdint.h>
+
+using namespace sgd;
+
+namespace {
+
+constexpr int ABI_VERSION = 1;
+constexpr int MAX_DIM = 1 << 20;
+
+inline bool fmt_ok(int fmt) { return fmt == SGD_FMT_BLOCK128 || fmt == SGD_FMT_MX32; }
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// N, K of a weight: positive multiples of 128 within range.
+int check_nk(int N, int K) {
+  if (N <= 0 || K <= 0 || N > MAX_DIM || K > MAX_DIM) return SGD_EINVAL;
+  if ((N % 128) || (K % 128)) return SGD_EDIM;
+  return SGD_OK;
+}
+
+int check_weight(const sgd_weight* w) {
+  if (!w) return SGD_EINVAL;
+  if (!fmt_ok(w->fmt)) return SGD_EFMT;
+  if (w->reserved != 0) return SGD_EINVAL;
+  int rc = check_nk(w->N, w->K);
+  if (rc) return rc;
+  if (!w->codes || !w->scales) return SGD_EINVAL;
+  if (!al16(w->codes) || !al4(w->scales)) return SGD_EALIGN;
+  return SGD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sgd_status_str(int status) {
+  switch (status) {
+    case SGD_OK: return "ok";
+    case SGD_EINVAL: return "invalid argument (null pointer, size or row count out of range)";
+    case SGD_EALIGN: return "pointer not aligned as required";
+    case SGD_EDIM: return "dimension not a multiple of its tile size, or shapes do not chain";
+    case SGD_EWORKSPACE: return "workspace missing or too small";
+    case SGD_EFMT: return "unknown format or mixed formats";
+    case SGD_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int sgd_abi_version(void) { return ABI_VERSION; }
+
+size_t sgd_packed_codes_bytes(int fmt, int N, int K) {
+  if (!fmt_ok(fmt) || check_nk(N, K) != SGD_OK) return 0;
+  return (size_t)N * (size_t)K;
+}
+
+size_t sgd_packed_scales_bytes(int fmt, int N, int K) {
+  if (!fmt_ok(fmt) || check_nk(N, K) != SGD_OK) return 0;
+  if (fmt == SGD_FMT_BLOCK128) return (size_t)(N / 128) * (size_t)(K / 128) * 4;
+  const size_t kg = ((size_t)K / 128 + 3) / 4;
+  return (size_t)(N / 16) * kg * 256;
+}
+
+int sgd_quantize_pack_weight(int fmt, const uint16_t* w_bf16, int N, int K, void* codes_out,
+                             void* scales_out, void* stream) {
+  if (!fmt_ok(fmt)) return SGD_EFMT;
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!w_bf16 || !codes_out || !scales_out) return SGD_EINVAL;
+  if (!al16(w_bf16) || !al16(codes_out) || !al4(scales_out)) return SGD_EALIGN;
+  return launch_pack_weight(fmt, w_bf16, N, K, codes_out, scales_out, as_stream(stream));
+}
+
+int sgd_unpack_weight(const sgd_weight* w, uint8_t* codes_rowmajor, void* scales_logical, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (!codes_rowmajor || !scales_logical) return SGD_EINVAL;
+  if (!al16(codes_rowmajor) || !al4(scales_logical)) return SGD_EALIGN;
+  return launch_unpack_weight(w->fmt, static_cast<const uint8_t*>(w->codes), w->scales, w->N, w->K,
+                              codes_rowmajor, scales_logical, as_stream(stream));
+}
+
+int sgd_quantize_act(int fmt, const uint16_t* x_bf16, int M, int K, uint8_t* codes, void* scales,
+                     void* stream) {
+  if (!fmt_ok(fmt)) return SGD_EFMT;
+  if (M <= 0 || M > 65536 || K <= 0 || K > MAX_DIM) return SGD_EINVAL;
+  if (K % 128) return SGD_EDIM;
+  if (!x_bf16 || !codes || !scales) return SGD_EINVAL;
+  if (!al16(x_bf16) || !al16(codes) || !al4(scales)) return SGD_EALIGN;
+  return launch_quantize_act(fmt, x_bf16, M, K, codes, scales, as_stream(stream));
+}
+
+size_t sgd_gemm_workspace_bytes(int fmt, int M, int N, int K) {
+  if (!fmt_ok(fmt) || M <= 0 || M > SGD_MAX_M || check_nk(N, K) != SGD_OK) return 0;
+  return stream_workspace_bytes(fmt, M, K, 0, N, K, false);
+}
+
+size_t sgd_mlp_workspace_bytes(int fmt, int M, int d, int ffn) {
+  if (!fmt_ok(fmt) || M <= 0 || M > SGD_MAX_M || check_nk(ffn, d) != SGD_OK) return 0;
+  if (ffn > 32768) return 0;
+  return stream_workspace_bytes(fmt, M, d, ffn, d, ffn, true);
+}
+
+int sgd_workspace_clear(void* workspace, size_t bytes, void* stream) {
+  if (!workspace || bytes == 0) return SGD_EINVAL;
+  if (!al16(workspace) || (bytes % 16)) return SGD_EALIGN;
+  return launch_fill_zero(workspace, bytes, as_stream(stream));
+}
+
+int sgd_scaled_gemm(const uint16_t* x_bf16, int M, const sgd_weight* w, uint16_t* y_bf16,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (!x_bf16 || !y_bf16 || M <= 0 || M > SGD_MAX_M) return SGD_EINVAL;
+  if (!al16(x_bf16) || !al16(y_bf16)) return SGD_EALIGN;
+  if (!workspace) return SGD_EWORKSPACE;
+  if (!al16(workspace)) return SGD_EALIGN;
+  if (ws_bytes < stream_workspace_bytes(w->fmt, M, w->K, 0, w->N, w->K, false)) return SGD_EWORKSPACE;
+  Problem p{};
+  p.fmt = w->fmt;
+  p.M = M;
+  p.x = x_bf16;
+  p.K1 = w->K;
+  p.w2 = w;
+  p.y = y_bf16;
+  p.ws = workspace;
+  return launch_stream(p, as_stream(stream));
+}
+
+int sgd_fused_swiglu_mlp(const uint16_t* x_bf16, int M, const sgd_weight* gate, const sgd_weight* up,
+                         const sgd_weight* down, uint16_t* y_bf16, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  int rc;
+  if ((rc = check_weight(gate)) || (rc = check_weight(up)) || (rc = check_weight(down))) return rc;
+  if (gate->fmt != up->fmt || gate->fmt != down->fmt) return SGD_EFMT;
+  const int d = gate->K, F = gate->N;
+  if (up->N != F || up->K != d || down->N != d || down->K != F) return SGD_EDIM;
+  if (F > 32768) return SGD_EINVAL;
+  if (!x_bf16 || !y_bf16 || M <= 0 || M > SGD_MAX_M) return SGD_EINVAL;
+  if (!al16(x_bf16) || !al16(y_bf16)) return SGD_EALIGN;
+  if (!workspace) return SGD_EWORKSPACE;
+  if (!al16(workspace)) return SGD_EALIGN;
+  if (ws_bytes < stream_workspace_bytes(gate->fmt, M, d, F, d, F, true)) return SGD_EWORKSPACE;
+  Problem p{};
+  p.fmt = gate->fmt;
+  p.M = M;
+  p.x = x_bf16;
+  p.K1 = d;
+  p.gate = gate;
+  p.up = up;
+  p.w2 = down;
+  p.y = y_bf16;
+  p.ws = workspace;
+  return launch_stream(p, as_stream(stream));
+}
+
+int sgd_bf16_to_f32(const uint16_t* x_bf16, int M, int d, float* h, void* stream) {
+  if (!x_bf16 || !h || M <= 0 || d <= 0 || M > 65536 || d > MAX_DIM) return SGD_EINVAL;
+  if (d % 128) return SGD_EDIM;
+  if (!al16(x_bf16) || !al16(h)) return SGD_EALIGN;
+  return launch_bf16_to_f32(x_bf16, M, d, h, as_stream(stream));
+}
+
+int sgd_rmsnorm_bf16(const float* h, int M, int d, float eps, uint16_t* x_bf16, void* stream) {
+  if (!x_bf16 || !h || M <= 0 || d <= 0 || M > 65536 || d > MAX_DIM || !(eps >= 0.0f)) return SGD_EINVAL;
+  if (d % 128) return SGD_EDIM;
+  if (!al16(x_bf16) || !al16(h)) return SGD_EALIGN;
+  return launch_rmsnorm(h, M, d, eps, x_bf16, as_stream(stream));
+}
+
+int sgd_residual_add(float* h, const uint16_t* y_bf16, int M, int d, void* stream) {
+  if (!y_bf16 || !h || M <= 0 || d <= 0 || M > 65536 || d > MAX_DIM) return SGD_EINVAL;
+  if (d % 128) return SGD_EDIM;
+  if (!al16(y_bf16) || !al16(h)) return SGD_EALIGN;
+  return launch_residual_add(h, y_bf16, M, d, as_stream(stream));
+}
+
+int sgd_head_logits(const float* h, int M, int K, const uint16_t* w_bf16, int N, float* logits,
+                    void* stream) {
+  if (!h || !w_bf16 || !logits || M <= 0 || M > SGD_MAX_M) return SGD_EINVAL;
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!al16(h) || !al16(w_bf16) || !al16(logits)) return SGD_EALIGN;
+  return launch_head(h, M, K, w_bf16, N, logits, as_stream(stream));
+}
+
+int sgd_argmax_rows(const float* logits, int M, int N, int32_t* out, void* stream) {
+  if (!logits || !out || M <= 0 || N <= 0 || M > 65536 || N > (1 << 24)) return SGD_EINVAL;
+  if (!al4(logits) || !al4(out)) return SGD_EALIGN;
+  return launch_argmax(logits, M, N, out, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 / E4M3 / E8M0
+// conversions, wavefront reductions, the 128-element group quantizer and
+// the scaled fp8 MFMA wrapper.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgd {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+enum : int { FMT_BLOCK = 1, FMT_MX = 2 };
+
+constexpr int WAVE = 64;
+constexpr float E4M3_MAX = 448.0f;
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 (OCP OFP8): round to nearest, ties to even, saturate at +-448.
+// Integer formulation on the fp32 bit pattern: for |v| >= 2^-6 keep the top
+// 3 mantissa bits with round-half-even on the 20 dropped bits (a carry moves
+// into the exponent by itself) and rebias the exponent from 127 to 7; below
+// 2^-6 the codes are the integers round(|v| * 2^9) of the subnormal grid.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu; // |v| >= 448 (and inf): saturate
+  if (a >= 0x3C800000u) {                    // |v| >= 2^-6: normal code
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((r >> 20) - ((127u - 7u) << 3));
+  }
+  float f = __uint_as_float(a) * 512.0f;     // exact: scaling by 2^9
+  return sign | (uint32_t)__builtin_rintf(f);
+}
+
+// ---------------------------------------------------------------------------
+// Scale rules
+// ---------------------------------------------------------------------------
+// 128x128 / 1x128 block scale: fl32(amax / 448), 1 for an all-zero group.
+// hipcc's default fp32 division is correctly rounded (IEEE).
+__device__ __forceinline__ float block_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / E4M3_MAX;
+}
+
+// MX (OCP MX v1.0) shared exponent X = floor(log2(amax)) - 8, clamped to
+// [-127, 127]; -127 for amax == 0.  floor(log2) comes from the exponent
+// field (subnormals: from the position of the leading mantissa bit).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  uint32_t b = __float_as_uint(amax) & 0x7FFFFFFFu;
+  if (b == 0) return -127;
+  int e = (int)(b >> 23);
+  int fl = e ? e - 127 : (31 - __clz((int)b)) - 149;
+  int X = fl - 8;
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// 2^-X as an fp32 value, for X in [-127, 119] (exponent field 127 - X).
+__device__ __forceinline__ float pow2_neg(int X) { return __uint_as_float((uint32_t)(127 - X) << 23); }
+
+// 2^X as an fp32 value for X in [-126, 127]; 2^-127 (the E8M0 byte 0) is the
+// fp32 subnormal 0x00400000.
+__device__ __forceinline__ float pow2_pos(int X) {
+  return X >= -126 ? __uint_as_float((uint32_t)(X + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Value of an E4M3 code (finite codes; the NaN codes are never produced).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+// max over aligned groups of 16 lanes
+__device__ __forceinline__ float seg16_max(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Quantize one 128-element group of a row with one wavefront: lane l holds
+// elements 2l and 2l+1.  BLOCK: one fp32 scale for the whole group.
+// MX: lanes 16b..16b+15 form 32-element block b (b = 0..3), one E8M0 byte
+// each.  Returns the two codes packed in the low 16 bits (element 2l in the
+// low byte).  *scale_f (BLOCK) / *scale_e (MX, this lane's block) are set.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ uint32_t quant_pair(float v0, float v1, float* scale_f, uint32_t* scale_e) {
+  float am = fmaxf(fabsf(v0), fabsf(v1));
+  if (FMT == FMT_BLOCK) {
+    float s = block_scale(wave_max(am));
+    *scale_f = s;
+    return e4m3_encode(v0 / s) | (e4m3_encode(v1 / s) << 8);
+  } else {
+    int X = mx_exponent(seg16_max(am));
+    *scale_e = (uint32_t)(X + 127);
+    float m = pow2_neg(X);
+    return e4m3_encode(v0 * m) | (e4m3_encode(v1 * m) << 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scaled fp8 MFMA 16x16x128.  Operand order (measured on gfx950): lane l
+// holds row/column l % 16 with K = 16*(l/16)+[0,16) in bytes 0..15 and
+// K = 64+16*(l/16)+[0,16) in bytes 16..31; the E8M0 scale of lane l applies
+// to row/column l % 16, 32-wide K block l / 16.  D: lane l holds column
+// l % 16, rows 4*(l/16)+r in element r.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ v8i make_v8i(uint4 lo, uint4 hi) {
+  v8i r;
+  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup synchronisation (agent scope: L2 is per XCD, so releases
+// write back and acquires invalidate the non-coherent caches).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin (whole wavefront) until *p >= target, then acquire.
+__device__ __forceinline__ void wait_geq(const uint32_t* p, uint32_t target) {
+  while (load_agent(p) < target) __builtin_amdgcn_s_sleep(1);
+  fence_acquire();
+}
+
+}  // namespace sgd

@@ -1,0 +1,45 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/swiglu_decode.h"
+
+namespace sgd {
+
+// Kernel launchers (arguments already validated).  Return SGD_OK/SGD_EHIP.
+int launch_pack_weight(int fmt, const uint16_t* w, int N, int K, void* codes, void* scales,
+                       hipStream_t s);
+int launch_unpack_weight(int fmt, const uint8_t* codes, const void* scales, int N, int K,
+                         uint8_t* out_codes, void* out_scales, hipStream_t s);
+int launch_quantize_act(int fmt, const uint16_t* x, int M, int K, uint8_t* codes, void* scales,
+                        hipStream_t s);
+int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// Streaming GEMM / fused MLP.  `gate`/`up` are null for the plain GEMM.
+struct Problem {
+  int fmt;
+  int M;
+  const uint16_t* x;   // [M, K1]
+  int K1;              // d (MLP) or K (GEMM)
+  const sgd_weight* gate;
+  const sgd_weight* up;
+  const sgd_weight* w2;  // down [d, F] (MLP) or W [N, K] (GEMM)
+  uint16_t* y;         // [M, w2->N]
+  void* ws;
+};
+size_t stream_workspace_bytes(int fmt, int M, int K1, int F, int N, int K2, bool mlp);
+int launch_stream(const Problem& p, hipStream_t s);
+
+// Decode-stack glue.
+int launch_bf16_to_f32(const uint16_t* x, int M, int d, float* h, hipStream_t s);
+int launch_rmsnorm(const float* h, int M, int d, float eps, uint16_t* x, hipStream_t s);
+int launch_residual_add(float* h, const uint16_t* y, int M, int d, hipStream_t s);
+int launch_head(const float* h, int M, int K, const uint16_t* w, int N, float* out, hipStream_t s);
+int launch_argmax(const float* logits, int M, int N, int32_t* out, hipStream_t s);
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? SGD_OK : SGD_EHIP; }
+
+}  // namespace sgd

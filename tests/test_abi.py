@@ -1,0 +1,121 @@
+"""CPU tests of the C-ABI library: it loads without a GPU, exports every
+function the header declares, and rejects invalid arguments on the host
+(these calls return before touching the HIP runtime)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from swiglu_decode_amd import _lib
+from swiglu_decode_amd._lib import SgdWeight
+
+E = dict(OK=0, EINVAL=-1, EALIGN=-2, EDIM=-3, EWORKSPACE=-4, EFMT=-5, EHIP=-6)
+BLK, MX = 1, 2
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.load()
+
+
+def test_every_header_function_is_exported(L):
+    names = _lib.header_symbols()
+    assert len(names) >= 17
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(L, n)
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version(L):
+    for code in E.values():
+        assert L.sgd_status_str(code)
+    assert b"unknown" in L.sgd_status_str(12345)
+    assert L.sgd_abi_version() == 1
+
+
+def test_packed_sizes(L):
+    assert L.sgd_packed_codes_bytes(BLK, 256, 512) == 256 * 512
+    assert L.sgd_packed_scales_bytes(BLK, 256, 512) == 2 * 4 * 4
+    assert L.sgd_packed_scales_bytes(MX, 256, 512) == 256 * 512 // 32
+    # K = 256: two k-tiles padded to a group of four
+    assert L.sgd_packed_scales_bytes(MX, 256, 256) == (256 // 16) * 256
+    assert L.sgd_packed_codes_bytes(3, 256, 256) == 0
+    assert L.sgd_packed_codes_bytes(BLK, 200, 256) == 0
+    assert L.sgd_packed_codes_bytes(BLK, 0, 256) == 0
+
+
+def test_workspace_sizes(L):
+    a = L.sgd_mlp_workspace_bytes(MX, 1, 4096, 12288)
+    b = L.sgd_mlp_workspace_bytes(MX, 128, 4096, 12288)
+    assert 0 < a < b
+    assert L.sgd_mlp_workspace_bytes(MX, 129, 4096, 12288) == 0
+    assert L.sgd_mlp_workspace_bytes(MX, 0, 4096, 12288) == 0
+    assert L.sgd_mlp_workspace_bytes(MX, 1, 4000, 12288) == 0
+    assert L.sgd_gemm_workspace_bytes(BLK, 16, 6144, 2048) > 0
+    assert L.sgd_gemm_workspace_bytes(BLK, 16, 6144, 2000) == 0
+
+
+def _w(fmt=BLK, N=256, K=256, codes=0x1000, scales=0x2000, reserved=0):
+    return SgdWeight(fmt, N, K, reserved, codes, scales)
+
+
+P = ctypes.c_void_p
+
+
+def test_argument_errors_launch_nothing(L):
+    # pack
+    assert L.sgd_quantize_pack_weight(7, P(0x1000), 256, 256, P(0x1000), P(0x1000), None) == E["EFMT"]
+    assert L.sgd_quantize_pack_weight(BLK, P(0x1000), 200, 256, P(0x1000), P(0x1000), None) == E["EDIM"]
+    assert L.sgd_quantize_pack_weight(BLK, None, 256, 256, P(0x1000), P(0x1000), None) == E["EINVAL"]
+    assert L.sgd_quantize_pack_weight(BLK, P(0x1001), 256, 256, P(0x1000), P(0x1000), None) == E["EALIGN"]
+    assert L.sgd_quantize_pack_weight(BLK, P(0x1000), -128, 256, P(0x1000), P(0x1000), None) == E["EINVAL"]
+    # act quant
+    assert L.sgd_quantize_act(MX, P(0x1000), 0, 256, P(0x1000), P(0x1000), None) == E["EINVAL"]
+    assert L.sgd_quantize_act(MX, P(0x1000), 4, 100, P(0x1000), P(0x1000), None) == E["EDIM"]
+    assert L.sgd_quantize_act(MX, P(0x1000), 4, 256, P(0x1008), P(0x1000), None) == E["EALIGN"]
+    # unpack
+    w = _w(reserved=1)
+    assert L.sgd_unpack_weight(ctypes.byref(w), P(0x1000), P(0x1000), None) == E["EINVAL"]
+    w = _w(codes=0x1004)
+    assert L.sgd_unpack_weight(ctypes.byref(w), P(0x1000), P(0x1000), None) == E["EALIGN"]
+    # gemm
+    w = _w()
+    ws_need = L.sgd_gemm_workspace_bytes(BLK, 4, 256, 256)
+    assert L.sgd_scaled_gemm(P(0x1000), 0, ctypes.byref(w), P(0x1000), P(0x1000), ws_need, None) == E["EINVAL"]
+    assert L.sgd_scaled_gemm(P(0x1000), 129, ctypes.byref(w), P(0x1000), P(0x1000), ws_need, None) == E["EINVAL"]
+    assert L.sgd_scaled_gemm(P(0x1000), 4, None, P(0x1000), P(0x1000), ws_need, None) == E["EINVAL"]
+    assert L.sgd_scaled_gemm(P(0x1000), 4, ctypes.byref(w), P(0x1000), None, ws_need, None) == E["EWORKSPACE"]
+    assert L.sgd_scaled_gemm(P(0x1000), 4, ctypes.byref(w), P(0x1000), P(0x1000), ws_need - 1, None) == E["EWORKSPACE"]
+    assert L.sgd_scaled_gemm(P(0x1002), 4, ctypes.byref(w), P(0x1000), P(0x1000), ws_need, None) == E["EALIGN"]
+    bad = _w(fmt=9)
+    assert L.sgd_scaled_gemm(P(0x1000), 4, ctypes.byref(bad), P(0x1000), P(0x1000), ws_need, None) == E["EFMT"]
+    # fused mlp: shapes must chain, formats must agree
+    g, u, d = _w(N=512, K=256), _w(N=512, K=256), _w(N=256, K=512)
+    need = L.sgd_mlp_workspace_bytes(BLK, 4, 256, 512)
+    args = lambda g_, u_, d_, ws=need: L.sgd_fused_swiglu_mlp(
+        P(0x1000), 4, ctypes.byref(g_), ctypes.byref(u_), ctypes.byref(d_), P(0x1000), P(0x1000), ws, None)
+    assert args(g, u, _w(N=256, K=384)) == E["EDIM"]
+    assert args(g, _w(fmt=MX, N=512, K=256), d) == E["EFMT"]
+    assert args(g, u, d, need - 16) == E["EWORKSPACE"]
+    # glue
+    assert L.sgd_rmsnorm_bf16(P(0x1000), 4, 100, ctypes.c_float(1e-6), P(0x1000), None) == E["EDIM"]
+    assert L.sgd_rmsnorm_bf16(P(0x1000), 4, 128, ctypes.c_float(-1.0), P(0x1000), None) == E["EINVAL"]
+    assert L.sgd_head_logits(P(0x1000), 200, 256, P(0x1000), 256, P(0x1000), None) == E["EINVAL"]
+    assert L.sgd_argmax_rows(P(0x1000), 0, 10, P(0x1000), None) == E["EINVAL"]
+    assert L.sgd_workspace_clear(P(0x1000), 24, None) == E["EALIGN"]
+
+
+def test_binding_refuses_wrong_dtypes_without_gpu():
+    import torch
+    import swiglu_decode_amd as sgd
+    x = torch.zeros(4, 256, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        sgd.quantize_act(x, "block")
+    with pytest.raises(ValueError):
+        sgd.fmt_code("fp4")
