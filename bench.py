@@ -1,0 +1,220 @@
+"""Benchmark: fused FP8 SwiGLU MLP, µs/call and achieved HBM GB/s at M = 1/16/64/128.
+
+Workload: SwiGLU MLP with d=4096, ffn=12288, MXFP8 (1x32 UE8M0 scales on both
+operands), bf16 activations ~ N(0,1), weights N(0, 0.02), synthetic and seeded.
+One step = one fused_swiglu_mlp launch at each M in {1, 16, 64, 128}.
+
+Timing: the packed weights are copied R times (>= 1 GiB in total, four times
+the 256 MB Infinity Cache) and every launch uses the next copy, so weights are
+read cold from HBM.  For each M a HIP graph of R launches (one per copy) is
+captured and replayed; HIP events on the launch stream bracket the timed
+replays.  Algorithmic bytes per launch = fp8 weight codes + weight scales +
+bf16 x + bf16 y; intermediates and activation scales are not counted.
+
+Output: one JSON line (see the keys below).  `value` is the step's aggregate
+algorithmic bytes divided by its time, in GB/s.  `roofline` describes the
+M=16 launch (the ≥70 %-of-peak target case); `per_m` lists every M.
+`cpu_baseline` times the CPU oracle on a bounded sample on this host; the
+same oracle outputs are compared with the GPU outputs (`parity`).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_mlp_d4096_ffn12288_mx_m16_traffic.txt")
+KERNEL_SOURCES = ["swiglu_decode_amd/csrc/stream.hip", "swiglu_decode_amd/csrc/sgd_device.hpp"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Counter-measured HBM bytes per launch of the M=16 kernel, if the file
+    was taken with the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(M, d, F, scale_bytes):
+    return 3 * d * F + scale_bytes + 2 * M * d * 2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--ms", default="1,16,64,128")
+    ap.add_argument("--fmt", default="mx")
+    ap.add_argument("--d", type=int, default=4096)
+    ap.add_argument("--ffn", type=int, default=12288)
+    ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the MLP would shard over ffn with one all-reduce of y; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import swiglu_decode_amd as sgd
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ms = [int(m) for m in args.ms.split(",")]
+    d, F, fmt = args.d, args.ffn, args.fmt
+    wl = synth.Workload("bench", d, F, tuple(ms), (fmt,), 1003)
+    inp = synth.mlp_inputs(wl, max(ms))
+    x_all = inp["x"].to(dev)
+    pw0 = [sgd.quantize_pack_weight(inp[k].to(dev), fmt) for k in ("wg", "wu", "wd")]
+    scale_bytes = sum(int(p.scales.numel()) for p in pw0)
+    set_bytes = sum(int(p.codes.numel()) + int(p.scales.numel()) for p in pw0)
+    R = max(2, int(np.ceil(args.rotate_bytes / set_bytes)))
+    copies = [pw0] + [[sgd.PackedWeight(p.fmt, p.N, p.K, p.codes.clone(), p.scales.clone()) for p in pw0]
+                      for _ in range(R - 1)]
+    ws = sgd.Workspace(dev, sgd.mlp_workspace_bytes(fmt, max(ms), d, F))
+    xs = {m: x_all[:m].contiguous() for m in ms}
+    ys = {m: torch.empty((m, d), dtype=torch.bfloat16, device=dev) for m in ms}
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    graphs = {}
+    with torch.cuda.stream(stream):
+        for m in ms:  # eager warm-up on the capture stream (first-call host setup)
+            sgd.fused_swiglu_mlp(xs[m], *copies[0], out=ys[m], workspace=ws)
+        stream.synchronize()
+        for m in ms:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(R):
+                    sgd.fused_swiglu_mlp(xs[m], *copies[r], out=ys[m], workspace=ws)
+            graphs[m] = g
+    torch.cuda.synchronize()
+
+    per_m = {}
+    with torch.cuda.stream(stream):
+        for m in ms:
+            for _ in range(args.warmup):
+                graphs[m].replay()
+            stream.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(args.steps):
+                graphs[m].replay()
+            t1.record(stream)
+            t1.synchronize()
+            us = t0.elapsed_time(t1) * 1e3 / (args.steps * R)
+            b = algorithmic_bytes(m, d, F, scale_bytes)
+            per_m[m] = dict(us_per_call=round(us, 3), bytes=b, gbs=round(b / us / 1e3, 1),
+                            pct_of_peak=round(100.0 * b / us / 1e3 / HBM_PEAK_GBS, 1))
+    torch.cuda.synchronize()
+
+    step_us = sum(per_m[m]["us_per_call"] for m in ms)
+    step_bytes = sum(per_m[m]["bytes"] for m in ms)
+    value = step_bytes / step_us / 1e3
+
+    # outputs of the last replay, for the parity pairing below
+    y_out = {m: ys[m].float().cpu().numpy() for m in ms}
+
+    rm = 16 if 16 in ms else ms[0]
+    traffic = read_traffic() if rm == 16 and d == 4096 and F == 12288 and fmt == "mx" else None
+    roof = dict(bound="hbm", achieved=per_m[rm]["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(per_m[rm]["gbs"] / HBM_PEAK_GBS, 4),
+                traffic=traffic, m=rm, us_per_launch=per_m[rm]["us_per_call"],
+                algorithmic_bytes_per_launch=per_m[rm]["bytes"])
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(inp, ms, fmt, y_out, step_bytes)
+
+    out = {
+        "metric": "fused FP8 SwiGLU µs/call + achieved HBM GB/s (% of peak) at M=1/16/64/128",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"SwiGLU MLP d={d} ffn={F} {'MXFP8 1x32 UE8M0' if fmt == 'mx' else '128x128 block fp8'}, "
+                               f"one fused launch per M in {ms}",
+                   "d": d, "ffn": F, "fmt": fmt, "ms": ms, "weight_copies_rotated": R,
+                   "parallelism": "single GPU"},
+        "per_m": {str(m): per_m[m] for m in ms},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(inp, ms, fmt, y_out, step_bytes):
+    """Time the CPU oracle (as it stands) on a bounded sample: one MLP call at
+    M=1 and one at M=16 on the same workload, weights quantized beforehand
+    (the analogue of the offline pack, untimed).  Returns the baseline in the
+    bench's unit (algorithmic GB/s) and the GPU-vs-oracle parity of those
+    calls."""
+    import numpy as np
+    from oracle import ref
+    from synth import bf16_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    q = [ref.QWeight(bf16_to_f64(inp[k]), fmt) for k in ("wg", "wu", "wd")]
+    x = bf16_to_f64(inp["x"])
+    d = x.shape[1]
+    F = q[0].N
+    scale_bytes = sum(int(np.asarray(w.scales).nbytes) for w in q)
+    sample = [m for m in (1, 16) if m in ms] or [ms[0]]
+    t_tot, b_tot = 0.0, 0
+    parity = {}
+    for m in sample:
+        t0 = time.perf_counter()
+        y = ref.swiglu_mlp(x[:m], *q)
+        t_tot += time.perf_counter() - t0
+        b_tot += algorithmic_bytes(m, d, F, scale_bytes)
+        parity[str(m)] = dict(rel_fro=float(f"{ref.rel_fro(y_out[m], y):.3e}"),
+                              max_abs_ratio=float(f"{ref.max_abs_ratio(y_out[m], y):.3e}"))
+    cpu = dict(value=round(b_tot / t_tot / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+               sample=f"one oracle MLP call at M={sample} (x quantization, fp64 dequantize + matmuls, "
+                      f"SwiGLU, re-quantization), weights pre-quantized; {t_tot:.1f} s on this host")
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    main()

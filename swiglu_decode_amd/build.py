@@ -20,8 +20,10 @@ ARCH = "gfx950"
 # -packed-fp32-ops off: hand-free of v_pk_{add,mul,fma}_f32 (see the design
 # notes); correctly rounded fp32 division and IEEE denormals are required for
 # bit-exact quantization.
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
+    f"-I{INCLUDE}",
     "-O3",
     "-std=c++17",
     "-fPIC",

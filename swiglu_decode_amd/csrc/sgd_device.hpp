@@ -142,11 +142,42 @@ __device__ __forceinline__ v8i make_v8i(uint4 lo, uint4 hi) {
 }
 
 // ---------------------------------------------------------------------------
-// Cross-workgroup synchronisation (agent scope: L2 is per XCD, so releases
-// write back and acquires invalidate the non-coherent caches).
+// Cross-workgroup communication.
+//
+// L2 is per XCD and not coherent across XCDs; the agent-scope fences of the
+// language memory model write back / invalidate a whole L2 each, which costs
+// far too much when issued per work item.  Instead:
+//  * every intermediate another workgroup reads is written with agent-
+//    coherent (sc1, write-through) stores, and a producer waits for all its
+//    stores to complete (s_waitcnt vmcnt(0)) before it arrives on a counter
+//    or raises a flag with an atomic;
+//  * small per-group data (scales, fp32 partial sums, the SwiGLU output) is
+//    read back with agent-coherent (sc1) loads;
+//  * the large activation operands are read with ordinary cached loads: each
+//    such region is written once per launch, read only after its flag, and
+//    laid out so that no 128-byte line straddles two groups, so no cache can
+//    hold a stale copy of it (caches are invalidated at kernel boundaries).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void st_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+// Wait until every memory operation this wavefront issued has completed.
+__device__ __forceinline__ void drain_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -157,10 +188,25 @@ __device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin (whole wavefront) until *p >= target, then acquire.
+// Spin (whole wavefront) until *p >= target.  The signal fence keeps the
+// compiler from moving later loads above the poll; the hardware issues them
+// only after the poll's value has been compared.
 __device__ __forceinline__ void wait_geq(const uint32_t* p, uint32_t target) {
-  while (load_agent(p) < target) __builtin_amdgcn_s_sleep(1);
-  fence_acquire();
+  while (load_agent(p) < target) __builtin_amdgcn_s_sleep(4);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Buffer resource over [base, base + bytes); loads through it with the sc1
+// cache policy are agent-coherent, and offsets past `bytes` read as zero.
+constexpr int AUX_SC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ v4f ld_coherent_v4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX_SC1));
+}
+__device__ __forceinline__ uint32_t ld_coherent_u8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, AUX_SC1);
 }
 
 }  // namespace sgd

@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/swiglu_decode.h"
+#include "swiglu_decode.h"
 
 namespace sgd {
 

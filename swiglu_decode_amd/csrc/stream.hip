@@ -101,10 +101,10 @@ struct Streamer {
   const uint32_t* bsm[NB];   // mx: packed scale dwords of n-tile nb for this lane, + (kt/4)*64
   const uint8_t* arow;       // A: lane's row (l%16) in m-tile 0, + 16*(l/16)
   size_t a_mt_stride;        // 16 * Kd
-  const float* asf;          // block: act scales + 4*(l/16), indexed kt*Mpad + 16*mt
-  int Mpad;
-  const uint8_t* asm8;       // mx: act scales of lane's row in m-tile 0, + l/16
-  size_t as_mt_stride;       // 16 * Kd/32
+  __amdgpu_buffer_rsrc_t asr; // activation scales (agent-coherent loads)
+  uint32_t as_off;           // lane's byte offset in it (block: 16*(l/16); mx: row*(Kd/32) + l/16)
+  uint32_t as_kt_stride;     // block: 4*Mpad; mx: 4
+  uint32_t as_mt_stride;     // block: 64; mx: 16*Kd/32
   int kt0, nk;
 
   v8i B[P][NB];
@@ -136,10 +136,11 @@ struct Streamer {
     for (int mt = 0; mt < MT; ++mt) {
       const uint8_t* p = ok ? arow + mt * a_mt_stride + (size_t)kt * 128 : ashared;
       a[mt] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+      const uint32_t so = as_off + (uint32_t)kt * as_kt_stride + (uint32_t)mt * as_mt_stride;
       if (FMT == FMT_BLOCK)
-        sxb[mt] = *reinterpret_cast<const v4f*>(asf + (size_t)kt * Mpad + 16 * mt);
+        sxb[mt] = ld_coherent_v4f(asr, so);
       else
-        sxm[mt] = asm8[mt * as_mt_stride + kt * 4];
+        sxm[mt] = ld_coherent_u8(asr, so);
     }
   }
 
@@ -353,6 +354,27 @@ struct DepthBf16 { static constexpr int P = MT <= 1 ? 3 : (MT <= 2 ? 2 : 1); };
 // ---------------------------------------------------------------------------
 // XQ item: quantize 128-wide groups [i*XQ_GPI, ...) of the padded x.
 // ---------------------------------------------------------------------------
+// Store one quantized 128-column group of one row with agent-coherent 32-bit
+// stores: codes (lane l holds elements 2l, 2l+1; even lanes write four) and
+// the group's scale(s) (block: one fp32 in [K/128][Mpad]; MX: four E8M0
+// bytes, one per 32-column block, as one word of [Mpad][K/32]).
+template <int FMT>
+__device__ __forceinline__ void store_group(uint8_t* codes_at_group, uint32_t c, float sf, uint32_t se,
+                                            float* sbl_at, uint8_t* smx_at) {
+  const int l = threadIdx.x & 63;
+  const uint32_t up = __shfl_down(c, 1, WAVE);
+  if ((l & 1) == 0) st_coherent(reinterpret_cast<uint32_t*>(codes_at_group + 2 * l), (c & 0xFFFFu) | (up << 16));
+  if (FMT == FMT_BLOCK) {
+    if (l == 0) st_coherent(sbl_at, sf);
+  } else {
+    const uint32_t e1 = __shfl(se, 16, WAVE), e2 = __shfl(se, 32, WAVE), e3 = __shfl(se, 48, WAVE);
+    if (l == 0) st_coherent(reinterpret_cast<uint32_t*>(smx_at), se | (e1 << 8) | (e2 << 16) | (e3 << 24));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// XQ item: quantize 128-wide groups [i*XQ_GPI, ...) of the padded x.
+// ---------------------------------------------------------------------------
 template <int FMT>
 __device__ void item_xq(const StreamArgs& a, int i) {
   const int w = wave_id(), l = threadIdx.x & 63;
@@ -368,23 +390,23 @@ __device__ void item_xq(const StreamArgs& a, int i) {
       const uint32_t pr = *reinterpret_cast<const uint32_t*>(a.x + off);
       c = quant_pair<FMT>(bf16_to_f32(pr & 0xFFFFu), bf16_to_f32(pr >> 16), &sf, &se);
     }
+    float* sbl = static_cast<float*>(a.xs) + (size_t)kg * a.Mpad + row;
+    uint8_t* smx = static_cast<uint8_t*>(a.xs) + (size_t)row * (a.K1 >> 5) + 4 * kg;
     if (a.mlp) {
       // exact bf16 of the dequantized value (block: code value, its fp32
       // group scale applied after the MFMA; MX: code value times 2^X)
       const float m = FMT == FMT_BLOCK ? 1.0f : pow2_pos((int)se - 127);
       const uint32_t lo = f32_to_bf16(e4m3_decode(c & 0xFFu) * m);
       const uint32_t hi = f32_to_bf16(e4m3_decode(c >> 8) * m);
-      *reinterpret_cast<uint32_t*>(a.xb + off) = lo | (hi << 16);
+      st_coherent(reinterpret_cast<uint32_t*>(a.xb + off), lo | (hi << 16));
+      if (FMT == FMT_BLOCK) {
+        if (l == 0) st_coherent(sbl, sf);
+      }
     } else {
-      *reinterpret_cast<uint16_t*>(a.xq + off) = (uint16_t)c;
-    }
-    if (FMT == FMT_BLOCK) {
-      if (l == 0) static_cast<float*>(a.xs)[(size_t)kg * a.Mpad + row] = sf;
-    } else if ((l & 15) == 0) {
-      static_cast<uint8_t*>(a.xs)[(size_t)row * (a.K1 >> 5) + 4 * kg + (l >> 4)] = (uint8_t)se;
+      store_group<FMT>(a.xq + (off - 2 * l), c, sf, se, sbl, smx);
     }
   }
-  fence_release();
+  drain_memory();
   __syncthreads();
   if (threadIdx.x == 0) atomic_add_agent(&a.ctrl[C_XQ], 1);
 }
@@ -397,32 +419,35 @@ __device__ void requant_group(const StreamArgs& a, int g) {
     uint32_t c = 0, se = 0;
     float sf = 1.0f;
     if (row < a.M) {
-      const float2 v = *reinterpret_cast<const float2*>(a.a32 + (size_t)row * a.F + g * 128 + 2 * l);
-      c = quant_pair<FMT>(v.x, v.y, &sf, &se);
+      const float* src = a.a32 + (size_t)row * a.F + g * 128 + 2 * l;
+      c = quant_pair<FMT>(ld_coherent(src), ld_coherent(src + 1), &sf, &se);
     }
-    *reinterpret_cast<uint16_t*>(a.aq + (size_t)row * a.F + g * 128 + 2 * l) = (uint16_t)c;
-    if (FMT == FMT_BLOCK) {
-      if (l == 0) static_cast<float*>(a.as)[(size_t)g * a.Mpad + row] = sf;
-    } else if ((l & 15) == 0) {
-      static_cast<uint8_t*>(a.as)[(size_t)row * (a.F >> 5) + 4 * g + (l >> 4)] = (uint8_t)se;
-    }
+    store_group<FMT>(a.aq + (size_t)row * a.F + g * 128, c, sf, se,
+                     static_cast<float*>(a.as) + (size_t)g * a.Mpad + row,
+                     static_cast<uint8_t*>(a.as) + (size_t)row * (a.F >> 5) + 4 * g);
   }
 }
 
 // Fill the A-operand pointers of a Streamer for a row-major [Mpad, Kd] code
-// matrix with scales in the internal layouts.
+// matrix (filler loads read the wavefront's own first k-tile, which is ready)
+// with scales in the internal layouts.
 template <class S, int FMT>
-__device__ __forceinline__ void set_a(S& st, const uint8_t* codes, const void* scales, int Kd, int Mpad) {
+__device__ __forceinline__ void set_a(S& st, const uint8_t* codes, const void* scales, int Kd, int Mpad,
+                                      int kt0) {
   const int l = threadIdx.x & 63;
   st.arow = codes + (size_t)(l & 15) * Kd + 16 * (l >> 4);
-  st.ashared = codes;
+  st.ashared = codes + (size_t)kt0 * 128;
   st.a_mt_stride = (size_t)16 * Kd;
-  st.Mpad = Mpad;
+  const uint32_t bytes = FMT == FMT_BLOCK ? (uint32_t)(Kd >> 7) * Mpad * 4 : (uint32_t)Mpad * (Kd >> 5);
+  st.asr = make_rsrc(scales, bytes);
   if (FMT == FMT_BLOCK) {
-    st.asf = static_cast<const float*>(scales) + 4 * (l >> 4);
+    st.as_off = 16 * (l >> 4);
+    st.as_kt_stride = 4 * Mpad;
+    st.as_mt_stride = 64;
   } else {
-    st.asm8 = static_cast<const uint8_t*>(scales) + (size_t)(l & 15) * (Kd >> 5) + (l >> 4);
-    st.as_mt_stride = (size_t)16 * (Kd >> 5);
+    st.as_off = (uint32_t)(l & 15) * (Kd >> 5) + (l >> 4);
+    st.as_kt_stride = 4;
+    st.as_mt_stride = 16 * (Kd >> 5);
   }
 }
 
@@ -493,7 +518,7 @@ __device__ void item_gu(const StreamArgs& a, int j, v4f* red, WgState& ws) {
       }
     }
     st.arow = a.xb + (size_t)(l & 15) * a.K1 + 16 * (l >> 4);
-    st.ashared = a.xb;
+    st.ashared = a.xb + (size_t)kt0 * 128;
     st.a_mt_stride = (size_t)16 * a.K1;
     st.Mpad = a.Mpad;
     if (FMT == FMT_BLOCK) st.asf = static_cast<const float*>(a.xs) + 4 * (l >> 4);
@@ -520,19 +545,18 @@ __device__ void item_gu(const StreamArgs& a, int j, v4f* red, WgState& ws) {
         const int row = mt * 16 + 4 * (l >> 4) + r;
         if (row < a.M) {
           const float g = acc[0][mt][r], u = acc[1][mt][r];
-          a.a32[(size_t)row * a.F + j * 16 + (l & 15)] = g / (1.0f + expf(-g)) * u;
+          st_coherent(a.a32 + (size_t)row * a.F + j * 16 + (l & 15), g / (1.0f + expf(-g)) * u);
         }
       }
-    fence_release();
+    drain_memory();
   }
   __syncthreads();
   const int grp = j >> 3;
   if (threadIdx.x == 0) ws.flag = (atomic_add_agent(&a.ctrl[a.off_grp + grp], 1) == 7u);
   __syncthreads();
   if (ws.flag) {
-    fence_acquire();
     requant_group<FMT>(a, grp);
-    fence_release();
+    drain_memory();
     __syncthreads();
     if (threadIdx.x == 0) {
       store_agent(&a.ctrl[a.off_grp + grp], 0u);
@@ -559,9 +583,9 @@ __device__ void item_dn(const StreamArgs& a, int i, v4f* red, WgState& ws) {
 #pragma unroll
   for (int s = 0; s < NTD; ++s) set_b<decltype(st), FMT>(st, s, a.w2, a.s2, dt * NTD + s, a.K2, kt0);
   if (a.mlp)
-    set_a<decltype(st), FMT>(st, a.aq, a.as, a.F, a.Mpad);
+    set_a<decltype(st), FMT>(st, a.aq, a.as, a.F, a.Mpad, kt0);
   else
-    set_a<decltype(st), FMT>(st, a.xq, a.xs, a.K1, a.Mpad);
+    set_a<decltype(st), FMT>(st, a.xq, a.xs, a.K1, a.Mpad, kt0);
   v4f acc[NTD][MT];
 #pragma unroll
   for (int nb = 0; nb < NTD; ++nb)
@@ -609,10 +633,10 @@ __device__ void item_dn(const StreamArgs& a, int i, v4f* red, WgState& ws) {
             if (a.n_kc == 1)
               a.y[(size_t)row * a.N + col] = (uint16_t)f32_to_bf16(acc[s][mt][r]);
             else
-              a.ypart[((size_t)kc * a.M + row) * a.N + col] = acc[s][mt][r];
+              st_coherent(a.ypart + ((size_t)kc * a.M + row) * a.N + col, acc[s][mt][r]);
           }
         }
-    if (a.n_kc > 1) fence_release();
+    if (a.n_kc > 1) drain_memory();
   }
   if (a.n_kc == 1) return;
   __syncthreads();
@@ -620,12 +644,11 @@ __device__ void item_dn(const StreamArgs& a, int i, v4f* red, WgState& ws) {
     ws.flag = (atomic_add_agent(&a.ctrl[a.off_ycnt + dt], 1) == (uint32_t)(a.n_kc - 1));
   __syncthreads();
   if (ws.flag) {
-    fence_acquire();
     constexpr int COLS = NTD * 16;
     for (int e = threadIdx.x; e < a.M * COLS; e += NW * 64) {
       const int row = e / COLS, col = dt * COLS + e % COLS;
       float v = 0.0f;
-      for (int c = 0; c < a.n_kc; ++c) v += a.ypart[((size_t)c * a.M + row) * a.N + col];
+      for (int c = 0; c < a.n_kc; ++c) v += ld_coherent(a.ypart + ((size_t)c * a.M + row) * a.N + col);
       a.y[(size_t)row * a.N + col] = (uint16_t)f32_to_bf16(v);
     }
     if (threadIdx.x == 0) store_agent(&a.ctrl[a.off_ycnt + dt], 0u);
@@ -646,6 +669,9 @@ __global__ __launch_bounds__(NW * 64, (MT >= 8 ? 1 : 2)) void stream_kernel(Stre
   __syncthreads();
   int ticket = blockIdx.x;
   while (ticket < a.total) {
+    // take the next ticket now; its latency overlaps this item
+    uint32_t next = 0;
+    if (threadIdx.x == 0) next = gridDim.x + atomic_add_agent(&a.ctrl[C_TICKET], 1);
     if (ticket < a.n_xq)
       item_xq<FMT>(a, ticket);
     else if (ticket < a.n_xq + a.n_gu)
@@ -653,14 +679,13 @@ __global__ __launch_bounds__(NW * 64, (MT >= 8 ? 1 : 2)) void stream_kernel(Stre
     else
       item_dn<MT, FMT>(a, ticket - a.n_xq - a.n_gu, red, ws);
     __syncthreads();
-    if (threadIdx.x == 0) ws.ticket = gridDim.x + atomic_add_agent(&a.ctrl[C_TICKET], 1);
+    if (threadIdx.x == 0) ws.ticket = next;
     __syncthreads();
     ticket = (int)uniform(ws.ticket);
   }
   if (threadIdx.x == 0) {
     if (atomic_add_agent(&a.ctrl[C_DONE], 1) == gridDim.x - 1) {
       // Every workgroup has taken its last ticket: reset the control block.
-      fence_acquire();
       const int n = a.off_ycnt + a.n_dt;
       for (int k = C_HDR; k < n; ++k) store_agent(&a.ctrl[k], 0u);
       store_agent(&a.ctrl[C_XQ], 0u);
