@@ -119,7 +119,9 @@ int sgd_scaled_gemm(const uint16_t* x_bf16, int M, const sgd_weight* w, uint16_t
   if (!al16(x_bf16) || !al16(y_bf16)) return SGD_EALIGN;
   if (!workspace) return SGD_EWORKSPACE;
   if (!al16(workspace)) return SGD_EALIGN;
-  if (ws_bytes < stream_workspace_bytes(w->fmt, M, w->K, 0, w->N, w->K, false)) return SGD_EWORKSPACE;
+  const size_t need = stream_workspace_bytes(w->fmt, M, w->K, 0, w->N, w->K, false);
+  if (need == 0) return SGD_EDIM;
+  if (ws_bytes < need) return SGD_EWORKSPACE;
   Problem p{};
   p.fmt = w->fmt;
   p.M = M;
@@ -144,7 +146,9 @@ int sgd_fused_swiglu_mlp(const uint16_t* x_bf16, int M, const sgd_weight* gate, 
   if (!al16(x_bf16) || !al16(y_bf16)) return SGD_EALIGN;
   if (!workspace) return SGD_EWORKSPACE;
   if (!al16(workspace)) return SGD_EALIGN;
-  if (ws_bytes < stream_workspace_bytes(gate->fmt, M, d, F, d, F, true)) return SGD_EWORKSPACE;
+  const size_t need = stream_workspace_bytes(gate->fmt, M, d, F, d, F, true);
+  if (need == 0) return SGD_EDIM;
+  if (ws_bytes < need) return SGD_EWORKSPACE;
   Problem p{};
   p.fmt = gate->fmt;
   p.M = M;

@@ -10,28 +10,36 @@
 // groups against 128x128 fp32 weight tiles, or 1x32 E8M0 on both operands),
 // fp32 accumulation and a bf16 result.
 //
-// How (gfx950 design).  At decode shapes (M <= 128) every weight byte is used
-// by at most 128 rows, so the work is a stream of HBM weight bytes into the
-// 16x16x128 scaled fp8 MFMA.  One persistent kernel walks a queue of work
-// items taken in ticket order:
-//   XQ  items  quantize x into the workspace (rows padded to 16 with zeros);
-//   GU  items  (MLP only) one 16-column slice of ffn: gate and up tiles over
-//              all of d, split over the 4 wavefronts of the workgroup, reduced
-//              in LDS, a = silu(g) * u written as fp32; the last of the 8 items
-//              of a 128-column group re-quantizes that group and raises its
-//              ready flag;
-//   DN  items  32 output columns x one K chunk of the second GEMM (down
-//              projection, or the plain GEMM's weight), split over the
-//              wavefronts; chunks of one column tile are summed in a fixed
-//              order by the last chunk to finish, then rounded to bf16.
-// Each wavefront keeps a ring of P k-tiles of weights (two 16-byte loads per
-// lane per 16x128 tile, fully coalesced) in flight.  Weight loads of an item
-// are issued before its dependency wait, so HBM stays busy while a consumer
-// waits for its producer.  Items depend only on items with smaller tickets,
-// tickets are handed out in order, and a workgroup only ever waits on items
-// already taken by running workgroups, so the queue cannot deadlock.  The
-// last workgroup to leave resets every counter, so the next call (or graph
-// replay) starts from a zeroed control block.
+// How (gfx950).  At decode shapes (M <= 128) the work is a stream of HBM
+// weight bytes into the matrix cores, and the time goes to keeping that
+// stream full and to the few points where workgroups must wait for each
+// other.  One persistent kernel, one workgroup per compute unit, a static
+// schedule:
+//   * A weight "band" is 16 rows of ffn for gate and up together (GU), or 32
+//     output columns of the second GEMM (DN: the down projection, or the
+//     plain GEMM's weight).  A band's k-tiles are cut into chunks of P
+//     k-tiles; each phase's chunks are dealt to workgroups in equal
+//     contiguous ranges, and within a workgroup round-robin to its streaming
+//     wavefronts.
+//   * Streaming wavefronts only load and multiply.  Each keeps a ring of P
+//     slots (two 16x128 weight tiles with their scales and the matching
+//     activation tile) in flight; a chunk's refills load the next chunk.  At
+//     the end of a band each streaming wavefront hands its partial sums to
+//     the workgroup's sync wavefront through LDS and goes on streaming: it
+//     never waits for memory writes.
+//   * The sync wavefront does everything that crosses workgroups: it
+//     quantizes its share of x, sums the streaming wavefronts' partials,
+//     combines the split-K partials of a band shared with a neighbouring
+//     workgroup (the last to arrive sums all of them in workgroup order, so
+//     results do not depend on timing), applies SiLU(gate)*up, re-quantizes
+//     each finished 128-column group of the product, raises the flags the
+//     second GEMM waits on, and writes the output.
+// Flags are written once per XCD (eight copies) so that at most the
+// workgroups of one XCD poll a cache line.  Every wait is on work that some
+// workgroup does before waiting itself, and all workgroups are resident
+// (the grid never exceeds what fits at once), so the waits always end.  The
+// last workgroup to finish clears the control block, so the next launch (or
+// graph replay) starts from zero.
 #include "sgd_device.hpp"
 #include "sgd_host.hpp"
 
@@ -39,14 +47,31 @@
 
 namespace sgd {
 
-constexpr int NW = 4;       // wavefronts per workgroup
-constexpr int NTD = 2;      // 16-row weight tiles per DN item
-constexpr int XQ_GPI = 32;  // 128-wide groups per XQ item
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-struct StreamArgs {
+// Per row-tile count MT (M rows padded to 16*MT): streaming wavefronts per
+// workgroup, ring depth (= k-tiles per chunk), LDS partial-sum slots.
+template <int MT>
+struct Cfg {
+  static constexpr int NS = MT >= 4 ? 3 : 7;
+  static constexpr int P = MT >= 8 ? 2 : 4;
+  static constexpr int NSLOT = 2;
+  static constexpr int NWAVE = NS + 1;
+};
+
+struct Phase {
+  int KT;       // k-tiles of the weight's K
+  int CPB;      // chunks per band, ceil(KT / P)
+  int nbands;   // GU: ffn / 16; DN: N / 32
+  int nchunks;  // nbands * CPB
+  int nwg;      // workgroups the chunks are dealt to
+};
+
+struct Args {
   int M, Mpad, mlp;
-  const uint16_t* x;
-  int K1;                    // columns of x
+  const uint16_t* x;         // [M, K1] bf16
+  int K1;
   const uint8_t* wg;         // gate / up packed codes [F, K1] (MLP)
   const void* sg;
   const uint8_t* wu;
@@ -55,313 +80,381 @@ struct StreamArgs {
   const uint8_t* w2;         // second GEMM weight [N, K2]
   const void* s2;
   int N, K2;
-  uint16_t* y;               // [M, N]
+  uint16_t* y;               // [M, N] bf16
   uint32_t* ctrl;
-  uint8_t* xq;               // [Mpad, K1] fp8 codes (plain GEMM)
-  uint16_t* xb;              // [Mpad, K1] bf16 widened quantized x (MLP; MX scale folded in)
-  void* xs;                  // block: fp32 [K1/128][Mpad]; mx: u8 [Mpad][K1/32]
-  float* a32;                // [M, F]
-  uint8_t* aq;               // [Mpad, F]
-  void* as;                  // block: fp32 [F/128][Mpad]; mx: u8 [Mpad][F/32]
-  float* ypart;              // [n_kc, M, N]
-  int n_xq, n_gu, n_dt, n_kc, ktc, total;
-  int off_grp, off_ready, off_ycnt;
+  uint8_t* xa;               // codes of Q(x) [M, K1]
+  void* xs;                  // x scales: block fp32 [K1/128][Mpad]; mx u8 [M][K1/32]
+  float* a32;                // [M, F] silu(g) * u
+  uint8_t* aq;               // [M, F] codes of Q(a)
+  void* as;                  // block fp32 [F/128][Mpad]; mx u8 [M][F/32]
+  float* gpart;              // [G][2][2][M][16] split-K partials of shared GU bands
+  float* dpart;              // [G][2][2][M][16] split-K partials of shared DN bands
+  uint32_t scale_bytes_g, scale_bytes_2;  // packed weight-scale sizes
+  int G;                     // workgroups in the grid
+  int n_pairs, n_items;      // x quantization: (k-group, row tile) pairs, dealt into items
+  int ngroups;               // F / 128
+  Phase gu, dn;
 };
 
-// Wavefront index within the workgroup, as a scalar (uniform) value so that
-// branches on it are scalar branches.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// Control block (32-bit words).  Page r (r < NREP) holds XCD copy r of the
+// x-quantization flags and of the group-ready flags.
+constexpr int C_DONE = 0;
+constexpr int PAGE0 = 1024, PAGE_WORDS = 1024, NREP = 8;
+constexpr int PG_XQ = 0, PG_RDY = 512;
+constexpr int C_GCNT = PAGE0 + NREP * PAGE_WORDS;  // arrivals of 16-column bands per group
+constexpr int C_GPCNT = C_GCNT + 512;              // arrivals on shared GU bands
+constexpr int C_DPCNT = C_GPCNT + 2048;            // arrivals on shared DN bands
+constexpr int CTRL_WORDS = 65536;
+constexpr size_t CTRL_BYTES = (size_t)CTRL_WORDS * 4;
+constexpr int MAX_ITEMS = 512, MAX_GROUPS = 512, MAX_GBANDS = 2048;
+// Workgroups a grid may have; the workspace holds two partial-sum slots for each.
+constexpr int MAX_WG = 512;
+constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past every buffer's end
 
-// Per-workgroup LDS state: the ticket broadcast, a flag broadcast, and what
-// this workgroup has already seen of its producers (so a consumer whose
-// inputs are known to be ready enters the pipeline without a global poll).
-struct WgState {
-  uint32_t ticket, flag;
-  uint32_t xq_seen;          // x quantization complete
-  uint32_t grp_seen[8];      // bit g: ffn group g re-quantized (ffn <= 32768)
-};
-
-__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Control block layout (uint32 words).
-constexpr int C_TICKET = 0, C_DONE = 1, C_XQ = 2, C_HDR = 16;
-
-// ---------------------------------------------------------------------------
-// The per-wavefront streaming loop.
-//   acc[nb][mt] += sum over k-tiles kt0..kt0+nk-1 of A(mt, kt) x B(nb, kt)^T
-// B(nb, kt): the packed tile at bt[nb] + k*2048 (k = kt - kt0).
-// A(mt, kt): rows 16mt..16mt+15 of a row-major [Mpad, Kd] code matrix.
-// ---------------------------------------------------------------------------
-template <int MT, int NB, int FMT, int P>
-struct Streamer {
-  const uint8_t* bt[NB];     // packed tile (nb, kt0), lane offset included
-  const uint8_t* bshared[NB];  // same tile without the lane offset (filler loads)
-  const uint8_t* ashared;    // row 0 of the A matrix at kt0 (filler loads)
-  const float* bsf[NB];      // block: weight-scale row of tile band nb, indexed by kt
-  const uint32_t* bsm[NB];   // mx: packed scale dwords of n-tile nb for this lane, + (kt/4)*64
-  const uint8_t* arow;       // A: lane's row (l%16) in m-tile 0, + 16*(l/16)
-  size_t a_mt_stride;        // 16 * Kd
-  __amdgpu_buffer_rsrc_t asr; // activation scales (agent-coherent loads)
-  uint32_t as_off;           // lane's byte offset in it (block: 16*(l/16); mx: row*(Kd/32) + l/16)
-  uint32_t as_kt_stride;     // block: 4*Mpad; mx: 4
-  uint32_t as_mt_stride;     // block: 64; mx: 16*Kd/32
-  int kt0, nk;
-
-  v8i B[P][NB];
-  v8i A[P][MT];
-  float SWb[P][NB];
-  v4f SXb[P][MT];
-  uint32_t SWm[P][NB];
-  uint32_t SXm[P][MT];
-
-  __device__ __forceinline__ void load_b(int slot_unused, int k, v8i (&b)[NB], float (&swb)[NB],
-                                         uint32_t (&swm)[NB]) {
-    (void)slot_unused;
-    const bool ok = k < nk;
-    const int kt = kt0 + (ok ? k : 0);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint8_t* p = ok ? bt[nb] + (size_t)k * 2048 : bshared[nb];
-      b[nb] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 1024));
-      if (FMT == FMT_BLOCK)
-        swb[nb] = bsf[nb][kt];
-      else
-        swm[nb] = bsm[nb][(kt >> 2) * 64];  // byte kt % 4 is selected at use
-    }
-  }
-  __device__ __forceinline__ void load_a(int k, v8i (&a)[MT], v4f (&sxb)[MT], uint32_t (&sxm)[MT]) {
-    const bool ok = k < nk;
-    const int kt = kt0 + (ok ? k : 0);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint8_t* p = ok ? arow + mt * a_mt_stride + (size_t)kt * 128 : ashared;
-      a[mt] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
-      const uint32_t so = as_off + (uint32_t)kt * as_kt_stride + (uint32_t)mt * as_mt_stride;
-      if (FMT == FMT_BLOCK)
-        sxb[mt] = ld_coherent_v4f(asr, so);
-      else
-        sxm[mt] = ld_coherent_u8(asr, so);
-    }
-  }
-
-  // Software pipeline over the wavefront's k-tiles.  The steady-state loop
-  // consumes slot s and refills it with the tile P steps ahead; every load in
-  // it is unconditional (past the last tile a slot is refilled from an
-  // address all lanes share, one cache line), so the hardware load counter
-  // sees the same pattern on every iteration and each consumer waits only
-  // for its own slot.  The prologue either issues the ring in that same
-  // order (dependency already known satisfied: `ready()` reads LDS only) or
-  // issues the weight loads, waits for the producer, loads the activations
-  // and drains, so the loop is entered either in the steady-state pattern or
-  // with nothing in flight.
-  template <class Ready, class Wait>
-  __device__ __forceinline__ void run(v4f (&acc)[NB][MT], Ready ready, Wait wait) {
-    if (nk <= 0) return;
-    if (ready()) {
-#pragma unroll
-      for (int s = 0; s < P; ++s) {
-        load_b(s, s, B[s], SWb[s], SWm[s]);
-        load_a(s, A[s], SXb[s], SXm[s]);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < P; ++s) load_b(s, s, B[s], SWb[s], SWm[s]);
-      wait();
-#pragma unroll
-      for (int s = 0; s < P; ++s) load_a(s, A[s], SXb[s], SXm[s]);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-    int base = 0;
-    for (; base + P <= nk; base += P) {
-#pragma unroll
-      for (int s = 0; s < P; ++s) {
-        step(s, base + s, acc);
-        load_b(s, base + s + P, B[s], SWb[s], SWm[s]);
-        load_a(base + s + P, A[s], SXb[s], SXm[s]);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < P; ++s)
-      if (base + s < nk) step(s, base + s, acc);
-  }
-
-  __device__ __forceinline__ void step(int s, int k, v4f (&acc)[NB][MT]) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (FMT == FMT_BLOCK) {
-          const v4f z = {0.f, 0.f, 0.f, 0.f};
-          const v4f t = mfma_f8(A[s][mt], B[s][nb], z, 127, 127);
-          acc[nb][mt] += t * (SXb[s][mt] * SWb[s][nb]);
-        } else {
-          const int sw = (int)(SWm[s][nb] >> (8 * ((kt0 + k) & 3)));
-          acc[nb][mt] = mfma_f8(A[s][mt], B[s][nb], acc[nb][mt], (int)SXm[s][mt], sw);
-        }
-      }
-    }
-  }
-};
-
-template <int MT>
-struct Depth { static constexpr int P = MT <= 2 ? 4 : 2; };
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // ---------------------------------------------------------------------------
-// The gate/up variant of the streaming loop.  The fp8 matrix instruction sums
-// its products in groups of 8 with only ~13 bits kept below the largest
-// product of a group (measured on gfx950), a ~1e-5 relative error that is
-// harmless in a final output but flips fp8 codes when the result is
-// re-quantized.  So the gate/up GEMM widens its fp8 operands to bf16 (exact:
-// E4M3 values fit in bf16; for MX the power-of-two scale is folded in, also
-// exactly) and runs the bf16 16x16x32 instruction, whose sums are fp32
-// accurate.  Weights arrive packed exactly as for the fp8 path; activations
-// come pre-widened (xb).  Operand order: value i of the lane's 32-byte run
-// goes to element i%8 of instruction i/8, for both operands.
+// static schedule
 // ---------------------------------------------------------------------------
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ v8bf widen8(uint32_t d0, uint32_t d1, float scale) {
-  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false);
-  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true);
-  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false);
-  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true);
-  v8bf r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+__device__ __forceinline__ int range_start(const Phase& ph, int W) {
+  return (int)(((long long)W * ph.nchunks) / ph.nwg);
+}
+// The workgroup whose range holds chunk c.
+__device__ __forceinline__ int owner_wg(const Phase& ph, int c) {
+  int W = (int)(((long long)c * ph.nwg) / ph.nchunks);
+  while (W + 1 < ph.nwg && range_start(ph, W + 1) <= c) ++W;
+  return W;
+}
+// Which of its two partial slots workgroup W uses for band b (0: the band
+// its range starts in, 1: the band it ends in).
+__device__ __forceinline__ int band_side(const Phase& ph, int W, int b) {
+  return b == range_start(ph, W) / ph.CPB ? 0 : 1;
 }
 
-__device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+struct ChunkPos {
+  int ok;    // a real chunk (else every load is a filler)
+  int band;
+  int kt0;   // first k-tile
+};
 
-template <int MT, int NB, int FMT, int P>
-struct StreamerBf16 {
-  const uint8_t* bt[NB];       // packed tile (nb, kt0), lane offset included
-  const uint8_t* bshared[NB];  // same tile without the lane offset (filler loads)
-  const float* bsf[NB];        // block: weight-scale row of tile band nb, indexed by kt
-  const uint32_t* bsm0[NB];    // mx: scale dwords of (row, block q/2), + (kt/4)*64
-  const uint32_t* bsm1[NB];    // mx: scale dwords of (row, block 2+q/2)
-  const uint16_t* arow;        // A: lane's row in m-tile 0 of xb, + 16*(l/16)
-  const uint16_t* ashared;     // row 0 of xb (filler loads)
-  size_t a_mt_stride;          // 16 * Kd (elements)
-  const float* asf;            // block: act scales + 4*(l/16), indexed kt*Mpad + 16*mt
-  int Mpad;
-  int kt0, nk;
+template <int P>
+__device__ __forceinline__ ChunkPos chunk_pos(const Phase& ph, int c, int c1) {
+  ChunkPos p{0, 0, 0};
+  if (c < c1) {
+    p.ok = 1;
+    p.band = c / ph.CPB;
+    p.kt0 = (c - p.band * ph.CPB) * P;
+  }
+  return p;
+}
 
-  v8i B[P][NB];
-  uint4 A[P][MT][4];
-  float SWb[P][NB];
-  v4f SXb[P][MT];
-  uint32_t SW0[P][NB], SW1[P][NB];
+// ---------------------------------------------------------------------------
+// LDS shared by a workgroup's wavefronts
+// ---------------------------------------------------------------------------
+template <int MT, int NS, int NSLOT>
+struct Lds {
+  v4f part[NSLOT][NS][2][MT][64];  // per band: each streaming wavefront's accumulators
+  uint32_t arrived[NSLOT];         // streaming wavefronts that filled the slot
+  uint32_t consumed;               // band events the sync wavefront has taken
+  uint32_t xq_ok;                  // Q(x) complete
+  uint32_t dn_ok;                  // the groups of Q(a) this workgroup reads are ready
+};
 
-  __device__ __forceinline__ void load_b(int k, v8i (&b)[NB], float (&swb)[NB], uint32_t (&sw0)[NB],
-                                         uint32_t (&sw1)[NB]) {
-    const bool ok = k < nk;
-    const int kt = kt0 + (ok ? k : 0);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint8_t* p = ok ? bt[nb] + (size_t)k * 2048 : bshared[nb];
-      b[nb] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 1024));
-      if (FMT == FMT_BLOCK) {
-        swb[nb] = bsf[nb][kt];
+__device__ __forceinline__ uint32_t lds_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_wait_geq(const uint32_t* p, uint32_t target) {
+  while (lds_load(p) < target) __builtin_amdgcn_s_sleep(1);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming wavefront
+// ---------------------------------------------------------------------------
+template <int MT, int FMT, int P>
+struct Streamer {
+  const Args& a;
+  const int q;  // index among the workgroup's streaming wavefronts
+  // ring: weights of stream 0/1 and their scale words (block: fp32 bits in
+  // S0; mx: S0/S1 = dwords holding this lane's two 32-column-block scales for
+  // gate/up, its own scale slot for the second GEMM), fp8 activations (one
+  // 32-byte operand per m-tile) and their scales (block: rows 4*(l/16)..+3
+  // as v4f; mx: gate/up: this lane's two 32-column-block bytes, second GEMM:
+  // its own scale slot in X0)
+  v8i RB[P][2];
+  uint32_t S0[P][2], S1[P][2];
+  v8i RA[P][MT];
+  v4f XB[P][MT];
+  uint32_t X0[P][MT], X1[P][MT];
+  // buffer resources of the current phase
+  __amdgpu_buffer_rsrc_t rw0, rw1, rs0, rs1, rx, rxs;
+  // lane constants
+  uint32_t lo16;                   // l * 16
+  uint32_t mo_gu0, mo_gu1, mo_dn;  // mx weight-scale lane offsets (bytes)
+  uint32_t xa_lane, aq_lane;       // activation lane offsets (bytes), m-tile 0, k-tile 0
+  uint32_t xs_lane, as_lane;       // activation-scale lane offsets (bytes)
+  int KdA;                         // row length of the second GEMM's activation
+
+  __device__ Streamer(const Args& args, int wq) : a(args), q(wq) {
+    const int l = lane_id();
+    lo16 = (uint32_t)l * 16u;
+    mo_gu0 = ((uint32_t)(l & 15) + 16u * (uint32_t)((l >> 4) >> 1)) * 4u;
+    mo_gu1 = ((uint32_t)(l & 15) + 16u * (2u + (uint32_t)((l >> 4) >> 1))) * 4u;
+    mo_dn = (uint32_t)l * 4u;
+    const uint32_t KT1 = (uint32_t)(a.K1 >> 7);
+    KdA = a.mlp ? a.F : a.K1;
+    xa_lane = (uint32_t)(l & 15) * (uint32_t)a.K1 + 16u * (uint32_t)(l >> 4);
+    aq_lane = (uint32_t)(l & 15) * (uint32_t)KdA + 16u * (uint32_t)(l >> 4);
+    if (FMT == FMT_BLOCK) {
+      xs_lane = 16u * (uint32_t)(l >> 4);
+      as_lane = 16u * (uint32_t)(l >> 4);
+    } else {
+      // gate/up: blocks (l/16)/2 and 2 + (l/16)/2 of row l%16; second GEMM: block l/16
+      xs_lane = (uint32_t)(l & 15) * (KT1 * 4u) + (uint32_t)((l >> 4) >> 1);
+      as_lane = (uint32_t)(l & 15) * (uint32_t)(KdA >> 5) + (uint32_t)(l >> 4);
+    }
+  }
+
+  __device__ __forceinline__ void make_resources(bool gu) {
+    const uint32_t KT1 = (uint32_t)(a.K1 >> 7);
+    const uint32_t xs_bytes = FMT == FMT_BLOCK ? KT1 * (uint32_t)a.Mpad * 4u : (uint32_t)a.M * (KT1 * 4u);
+    if (gu) {
+      const uint32_t bytes_g = (uint32_t)a.F * (uint32_t)a.K1;
+      rw0 = make_rsrc(a.wg, bytes_g);
+      rw1 = make_rsrc(a.wu, bytes_g);
+      rs0 = make_rsrc(a.sg, a.scale_bytes_g);
+      rs1 = make_rsrc(a.su, a.scale_bytes_g);
+      rx = make_rsrc(a.xa, (uint32_t)a.M * (uint32_t)a.K1);
+      rxs = make_rsrc(a.xs, xs_bytes);
+    } else {
+      rw0 = rw1 = make_rsrc(a.w2, (uint32_t)a.N * (uint32_t)a.K2);
+      rs0 = rs1 = make_rsrc(a.s2, a.scale_bytes_2);
+      if (a.mlp) {
+        rx = make_rsrc(a.aq, (uint32_t)a.M * (uint32_t)a.F);
+        rxs = make_rsrc(a.as, FMT == FMT_BLOCK ? (uint32_t)(a.F >> 7) * (uint32_t)a.Mpad * 4u
+                                              : (uint32_t)a.M * (uint32_t)(a.F >> 5));
       } else {
-        sw0[nb] = bsm0[nb][(kt >> 2) * 64];
-        sw1[nb] = bsm1[nb][(kt >> 2) * 64];
+        rx = make_rsrc(a.xa, (uint32_t)a.M * (uint32_t)a.K1);
+        rxs = make_rsrc(a.xs, xs_bytes);
       }
     }
   }
-  __device__ __forceinline__ void load_a(int k, uint4 (&a)[MT][4], v4f (&sxb)[MT]) {
-    const bool ok = k < nk;
-    const int kt = kt0 + (ok ? k : 0);
+
+  static __device__ __forceinline__ uint4 ld4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+
+  // ---- loads of one ring slot (unconditional: fillers read past the end) ----
+  template <bool GU>
+  __device__ __forceinline__ void load_b(int s, const ChunkPos& cp, int KT, int k) {
+    const int kt_ = cp.kt0 + k;
+    const bool ok = cp.ok && kt_ < KT;
+    const uint32_t kt = ok ? (uint32_t)kt_ : 0u;
+    const uint32_t n0 = GU ? (uint32_t)cp.band : 2u * (uint32_t)cp.band;
+    const uint32_t n1 = GU ? (uint32_t)cp.band : 2u * (uint32_t)cp.band + 1u;
+    const uint32_t uKT = (uint32_t)KT;
+    const uint32_t t0 = ok ? (n0 * uKT + kt) * 2048u + lo16 : OOB;
+    const uint32_t t1 = ok ? (n1 * uKT + kt) * 2048u + lo16 : OOB;
+    RB[s][0] = make_v8i(ld4(rw0, t0), ld4(rw0, t0 + 1024u));
+    RB[s][1] = make_v8i(ld4(rw1, t1), ld4(rw1, t1 + 1024u));
+    if (FMT == FMT_BLOCK) {
+      const uint32_t o0 = ok ? ((n0 >> 3) * uKT + kt) * 4u : OOB;
+      const uint32_t o1 = ok ? ((n1 >> 3) * uKT + kt) * 4u : OOB;
+      S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, o0, 0, 0);
+      S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, o1, 0, 0);
+    } else {
+      const uint32_t KG = (uKT + 3u) >> 2;
+      const uint32_t g0 = (n0 * KG + (kt >> 2)) * 256u;
+      const uint32_t g1 = (n1 * KG + (kt >> 2)) * 256u;
+      if (GU) {
+        S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_gu0 : OOB, 0, 0);
+        S1[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_gu1 : OOB, 0, 0);
+        S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_gu0 : OOB, 0, 0);
+        S1[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_gu1 : OOB, 0, 0);
+      } else {
+        S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_dn : OOB, 0, 0);
+        S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_dn : OOB, 0, 0);
+      }
+    }
+  }
+
+  template <bool GU>
+  __device__ __forceinline__ void load_a(int s, const ChunkPos& cp, int KT, int k) {
+    const int kt_ = cp.kt0 + k;
+    const bool ok = cp.ok && kt_ < KT;
+    const uint32_t kt = ok ? (uint32_t)kt_ : 0u;
+    const uint32_t Kd = GU ? (uint32_t)a.K1 : (uint32_t)KdA;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* p = ok ? arow + mt * a_mt_stride + (size_t)kt * 128 : ashared;
-      const uint4* q = reinterpret_cast<const uint4*>(p);
-      a[mt][0] = q[0];
-      a[mt][1] = q[1];
-      a[mt][2] = q[8];   // + 64 elements
-      a[mt][3] = q[9];
-      if (FMT == FMT_BLOCK) sxb[mt] = *reinterpret_cast<const v4f*>(asf + (size_t)kt * Mpad + 16 * mt);
+      const uint32_t o = ok ? (GU ? xa_lane : aq_lane) + (uint32_t)mt * 16u * Kd + kt * 128u : OOB;
+      RA[s][mt] = make_v8i(ld4(rx, o), ld4(rx, ok ? o + 64u : OOB));
+      if (FMT == FMT_BLOCK) {
+        const uint32_t so = (GU ? xs_lane : as_lane) + (kt * (uint32_t)a.Mpad + 16u * (uint32_t)mt) * 4u;
+        XB[s][mt] = ld_coherent_v4f(rxs, ok ? so : OOB);
+      } else {
+        const uint32_t so = (GU ? xs_lane : as_lane) + (uint32_t)mt * 16u * (Kd >> 5) + kt * 4u;
+        X0[s][mt] = ld_coherent_u8(rxs, ok ? so : OOB);
+        if (GU) X1[s][mt] = ld_coherent_u8(rxs, ok ? so + 2u : OOB);
+      }
     }
   }
 
-  __device__ __forceinline__ void step(int s, int k, v4f (&acc)[NB][MT]) {
-    const int sh = 8 * ((kt0 + k) & 3);
+  // ---- one k-step ------------------------------------------------------------
+  static __device__ __forceinline__ v8bf widen8(uint32_t d0, uint32_t d1, float scale) {
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true);
+    v8bf v;
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+    return v;
+  }
+
+  // Gate/up: fp8 widened to bf16 (exact; MX scale folded in), bf16 MFMA.  The
+  // fp8 matrix instruction sums its products in groups of 8 keeping only
+  // ~13 bits below the largest product of a group (measured on gfx950); that
+  // ~1e-5 relative error would flip fp8 codes of the re-quantized product,
+  // while the bf16 instruction's sums are fp32-accurate.
+  __device__ __forceinline__ void step_gu(int s, int kt, v4f (&acc)[2][MT]) {
+    const int sh = 8 * (kt & 3);
+    v8bf av[MT][4];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int mt = 0; mt < MT; ++mt) {
       float s0 = 1.0f, s1 = 1.0f;
       if (FMT == FMT_MX) {
-        s0 = pow2_pos((int)((SW0[s][nb] >> sh) & 0xFFu) - 127);
-        s1 = pow2_pos((int)((SW1[s][nb] >> sh) & 0xFFu) - 127);
+        s0 = pow2_pos((int)X0[s][mt] - 127);
+        s1 = pow2_pos((int)X1[s][mt] - 127);
       }
+      const v8i x = RA[s][mt];
+      av[mt][0] = widen8((uint32_t)x[0], (uint32_t)x[1], s0);
+      av[mt][1] = widen8((uint32_t)x[2], (uint32_t)x[3], s0);
+      av[mt][2] = widen8((uint32_t)x[4], (uint32_t)x[5], s1);
+      av[mt][3] = widen8((uint32_t)x[6], (uint32_t)x[7], s1);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float s0 = 1.0f, s1 = 1.0f;
+      if (FMT == FMT_MX) {
+        s0 = pow2_pos((int)((S0[s][nb] >> sh) & 0xFFu) - 127);
+        s1 = pow2_pos((int)((S1[s][nb] >> sh) & 0xFFu) - 127);
+      }
+      const v8i w = RB[s][nb];
       v8bf b[4];
-      b[0] = widen8((uint32_t)B[s][nb][0], (uint32_t)B[s][nb][1], s0);
-      b[1] = widen8((uint32_t)B[s][nb][2], (uint32_t)B[s][nb][3], s0);
-      b[2] = widen8((uint32_t)B[s][nb][4], (uint32_t)B[s][nb][5], s1);
-      b[3] = widen8((uint32_t)B[s][nb][6], (uint32_t)B[s][nb][7], s1);
+      b[0] = widen8((uint32_t)w[0], (uint32_t)w[1], s0);
+      b[1] = widen8((uint32_t)w[2], (uint32_t)w[3], s0);
+      b[2] = widen8((uint32_t)w[4], (uint32_t)w[5], s1);
+      b[3] = widen8((uint32_t)w[6], (uint32_t)w[7], s1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (FMT == FMT_BLOCK) {
           v4f t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(A[s][mt][i]), b[i], t, 0, 0, 0);
-          acc[nb][mt] += t * (SXb[s][mt] * SWb[s][nb]);
+          for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[i], t, 0, 0, 0);
+          acc[nb][mt] += t * (XB[s][mt] * __uint_as_float(S0[s][nb]));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(A[s][mt][i]), b[i], acc[nb][mt], 0, 0, 0);
+            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[i], acc[nb][mt], 0, 0, 0);
         }
       }
     }
   }
 
-  // Same pipeline discipline as Streamer::run.
-  template <class Ready, class Wait>
-  __device__ __forceinline__ void run(v4f (&acc)[NB][MT], Ready ready, Wait wait) {
-    if (nk <= 0) return;
-    if (ready()) {
+  // Second GEMM: scaled fp8 MFMA (MX scales in the instruction).
+  __device__ __forceinline__ void step_dn(int s, int kt, v4f (&acc)[2][MT]) {
+    const int sh = 8 * (kt & 3);
 #pragma unroll
-      for (int s = 0; s < P; ++s) {
-        load_b(s, B[s], SWb[s], SW0[s], SW1[s]);
-        load_a(s, A[s], SXb[s]);
-      }
-    } else {
+    for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-      for (int s = 0; s < P; ++s) load_b(s, B[s], SWb[s], SW0[s], SW1[s]);
-      wait();
-#pragma unroll
-      for (int s = 0; s < P; ++s) load_a(s, A[s], SXb[s]);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-    int base = 0;
-    for (; base + P <= nk; base += P) {
-#pragma unroll
-      for (int s = 0; s < P; ++s) {
-        step(s, base + s, acc);
-        load_b(base + s + P, B[s], SWb[s], SW0[s], SW1[s]);
-        load_a(base + s + P, A[s], SXb[s]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const v8i av = RA[s][mt];
+        if (FMT == FMT_BLOCK) {
+          const v4f z = {0.f, 0.f, 0.f, 0.f};
+          const v4f t = mfma_f8(av, RB[s][nb], z, 127, 127);
+          acc[nb][mt] += t * (XB[s][mt] * __uint_as_float(S0[s][nb]));
+        } else {
+          acc[nb][mt] = mfma_f8(av, RB[s][nb], acc[nb][mt], (int)X0[s][mt], (int)(S0[s][nb] >> sh));
+        }
       }
     }
+  }
+
+  // Hand this wavefront's sums for band event k to the sync wavefront.
+  template <int NS, int NSLOT>
+  __device__ __forceinline__ void publish(Lds<MT, NS, NSLOT>& L, int k, v4f (&acc)[2][MT]) {
+    const int slot = k % NSLOT;
+    if (k >= NSLOT) lds_wait_geq(&L.consumed, (uint32_t)(k - NSLOT + 1));
 #pragma unroll
-    for (int s = 0; s < P; ++s)
-      if (base + s < nk) step(s, base + s, acc);
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) L.part[slot][q][nb][mt][lane_id()] = acc[nb][mt];
+    if (lane_id() == 0)
+      __hip_atomic_fetch_add(&L.arrived[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+
+  // Stream this workgroup's chunks of one phase.
+  template <bool GU, int NS, int NSLOT>
+  __device__ __forceinline__ void run_phase(Lds<MT, NS, NSLOT>& L, int& k) {
+    const Phase& ph = GU ? a.gu : a.dn;
+    const int W = blockIdx.x;
+    if (W >= ph.nwg) return;
+    const int c0 = range_start(ph, W), c1 = range_start(ph, W + 1);
+    if (c0 >= c1) return;
+    const int KT = ph.KT;
+    make_resources(GU);
+    int c = c0 + q;
+    ChunkPos cp = chunk_pos<P>(ph, c, c1);
+#pragma unroll
+    for (int s = 0; s < P; ++s) load_b<GU>(s, cp, KT, s);
+    // activations only once they exist
+    lds_wait_geq(GU || !a.mlp ? &L.xq_ok : &L.dn_ok, 1u);
+#pragma unroll
+    for (int s = 0; s < P; ++s) load_a<GU>(s, cp, KT, s);
+    const int bf = c0 / ph.CPB, bl = (c1 - 1) / ph.CPB;
+    for (int b = bf; b <= bl; ++b) {
+      const int hi = min(c1, (b + 1) * ph.CPB);
+      v4f acc[2][MT];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+      while (c < hi) {
+        const int cn = c + NS;
+        const ChunkPos np = chunk_pos<P>(ph, cn, c1);
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+          const int kt = cp.kt0 + s;
+          if (kt < KT) {
+            if (GU)
+              step_gu(s, kt, acc);
+            else
+              step_dn(s, kt, acc);
+          }
+          load_b<GU>(s, np, KT, s);
+          load_a<GU>(s, np, KT, s);
+        }
+        c = cn;
+        cp = np;
+      }
+      publish(L, k++, acc);
+    }
   }
 };
 
-template <int MT>
-struct DepthBf16 { static constexpr int P = MT <= 1 ? 3 : (MT <= 2 ? 2 : 1); };
-
 // ---------------------------------------------------------------------------
-// XQ item: quantize 128-wide groups [i*XQ_GPI, ...) of the padded x.
+// Sync wavefront
 // ---------------------------------------------------------------------------
 // Store one quantized 128-column group of one row with agent-coherent 32-bit
 // stores: codes (lane l holds elements 2l, 2l+1; even lanes write four) and
-// the group's scale(s) (block: one fp32 in [K/128][Mpad]; MX: four E8M0
-// bytes, one per 32-column block, as one word of [Mpad][K/32]).
+// the group's scale(s).
 template <int FMT>
 __device__ __forceinline__ void store_group(uint8_t* codes_at_group, uint32_t c, float sf, uint32_t se,
                                             float* sbl_at, uint8_t* smx_at) {
-  const int l = threadIdx.x & 63;
+  const int l = lane_id();
   const uint32_t up = __shfl_down(c, 1, WAVE);
   if ((l & 1) == 0) st_coherent(reinterpret_cast<uint32_t*>(codes_at_group + 2 * l), (c & 0xFFFFu) | (up << 16));
   if (FMT == FMT_BLOCK) {
@@ -372,326 +465,285 @@ __device__ __forceinline__ void store_group(uint8_t* codes_at_group, uint32_t c,
   }
 }
 
-// ---------------------------------------------------------------------------
-// XQ item: quantize 128-wide groups [i*XQ_GPI, ...) of the padded x.
-// ---------------------------------------------------------------------------
-template <int FMT>
-__device__ void item_xq(const StreamArgs& a, int i) {
-  const int w = wave_id(), l = threadIdx.x & 63;
-  const int KG = a.K1 >> 7;
-  const int G = a.Mpad * KG;
-  const int g0 = i * XQ_GPI, g1 = min(G, g0 + XQ_GPI);
-  for (int g = g0 + w; g < g1; g += NW) {
-    const int row = g / KG, kg = g % KG;
-    const size_t off = (size_t)row * a.K1 + kg * 128 + 2 * l;
-    uint32_t c = 0, se = 0;
-    float sf = 1.0f;
-    if (row < a.M) {
-      const uint32_t pr = *reinterpret_cast<const uint32_t*>(a.x + off);
-      c = quant_pair<FMT>(bf16_to_f32(pr & 0xFFFFu), bf16_to_f32(pr >> 16), &sf, &se);
-    }
-    float* sbl = static_cast<float*>(a.xs) + (size_t)kg * a.Mpad + row;
-    uint8_t* smx = static_cast<uint8_t*>(a.xs) + (size_t)row * (a.K1 >> 5) + 4 * kg;
-    if (a.mlp) {
-      // exact bf16 of the dequantized value (block: code value, its fp32
-      // group scale applied after the MFMA; MX: code value times 2^X)
-      const float m = FMT == FMT_BLOCK ? 1.0f : pow2_pos((int)se - 127);
-      const uint32_t lo = f32_to_bf16(e4m3_decode(c & 0xFFu) * m);
-      const uint32_t hi = f32_to_bf16(e4m3_decode(c >> 8) * m);
-      st_coherent(reinterpret_cast<uint32_t*>(a.xb + off), lo | (hi << 16));
-      if (FMT == FMT_BLOCK) {
-        if (l == 0) st_coherent(sbl, sf);
-      }
-    } else {
-      store_group<FMT>(a.xq + (off - 2 * l), c, sf, se, sbl, smx);
-    }
-  }
-  drain_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) atomic_add_agent(&a.ctrl[C_XQ], 1);
+// Block-format scales live in [groups][Mpad]; rows M..Mpad-1 hold zero.
+__device__ __forceinline__ void zero_pad_scales(float* col_of_group, int M, int Mpad) {
+  const int l = lane_id();
+  if (l >= M && l < Mpad) st_coherent(col_of_group + l, 0.0f);
+  if (l + 64 >= M && l + 64 < Mpad) st_coherent(col_of_group + l + 64, 0.0f);
 }
 
-// Re-quantize 128-column group g of a32 into aq / as (all Mpad rows).
+// Quantize x for one item: its (128-column group, 16-row tile) pairs.
 template <int FMT>
-__device__ void requant_group(const StreamArgs& a, int g) {
-  const int w = wave_id(), l = threadIdx.x & 63;
-  for (int row = w; row < a.Mpad; row += NW) {
-    uint32_t c = 0, se = 0;
-    float sf = 1.0f;
-    if (row < a.M) {
-      const float* src = a.a32 + (size_t)row * a.F + g * 128 + 2 * l;
-      c = quant_pair<FMT>(ld_coherent(src), ld_coherent(src + 1), &sf, &se);
+__device__ __forceinline__ void xq_item(const Args& a, int item) {
+  const int l = lane_id();
+  const int MTa = a.Mpad >> 4;
+  const int p0 = (int)(((long long)item * a.n_pairs) / a.n_items);
+  const int p1 = (int)(((long long)(item + 1) * a.n_pairs) / a.n_items);
+  for (int p = p0; p < p1; ++p) {
+    const int kg = p / MTa, mt = p - kg * MTa;
+    const int r0 = mt * 16, nr = min(16, a.M - r0);
+    uint32_t pr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      pr[i] = *reinterpret_cast<const uint32_t*>(a.x + (size_t)min(r0 + i, a.M - 1) * a.K1 + kg * 128 + 2 * l);
+    float* sbl = static_cast<float*>(a.xs) + (size_t)kg * a.Mpad;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < nr) {
+        const int row = r0 + i;
+        float sf = 1.0f;
+        uint32_t se = 0;
+        const uint32_t c = quant_pair<FMT>(bf16_to_f32(pr[i] & 0xFFFFu), bf16_to_f32(pr[i] >> 16), &sf, &se);
+        store_group<FMT>(a.xa + (size_t)row * a.K1 + kg * 128, c, sf, se, sbl + row,
+                         static_cast<uint8_t*>(a.xs) + (size_t)row * (a.K1 >> 5) + 4 * kg);
+      }
     }
+    if (FMT == FMT_BLOCK && mt == MTa - 1) zero_pad_scales(sbl, a.M, a.Mpad);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void requant_group(const Args& a, int g) {
+  for (int row = 0; row < a.M; ++row) {
+    const float* src = a.a32 + (size_t)row * a.F + g * 128 + 2 * lane_id();
+    float sf = 1.0f;
+    uint32_t se = 0;
+    const uint32_t c = quant_pair<FMT>(ld_coherent(src), ld_coherent(src + 1), &sf, &se);
     store_group<FMT>(a.aq + (size_t)row * a.F + g * 128, c, sf, se,
                      static_cast<float*>(a.as) + (size_t)g * a.Mpad + row,
                      static_cast<uint8_t*>(a.as) + (size_t)row * (a.F >> 5) + 4 * g);
   }
+  if (FMT == FMT_BLOCK) zero_pad_scales(static_cast<float*>(a.as) + (size_t)g * a.Mpad, a.M, a.Mpad);
 }
 
-// Fill the A-operand pointers of a Streamer for a row-major [Mpad, Kd] code
-// matrix (filler loads read the wavefront's own first k-tile, which is ready)
-// with scales in the internal layouts.
-template <class S, int FMT>
-__device__ __forceinline__ void set_a(S& st, const uint8_t* codes, const void* scales, int Kd, int Mpad,
-                                      int kt0) {
-  const int l = threadIdx.x & 63;
-  st.arow = codes + (size_t)(l & 15) * Kd + 16 * (l >> 4);
-  st.ashared = codes + (size_t)kt0 * 128;
-  st.a_mt_stride = (size_t)16 * Kd;
-  const uint32_t bytes = FMT == FMT_BLOCK ? (uint32_t)(Kd >> 7) * Mpad * 4 : (uint32_t)Mpad * (Kd >> 5);
-  st.asr = make_rsrc(scales, bytes);
-  if (FMT == FMT_BLOCK) {
-    st.as_off = 16 * (l >> 4);
-    st.as_kt_stride = 4 * Mpad;
-    st.as_mt_stride = 64;
-  } else {
-    st.as_off = (uint32_t)(l & 15) * (Kd >> 5) + (l >> 4);
-    st.as_kt_stride = 4;
-    st.as_mt_stride = 16 * (Kd >> 5);
-  }
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Set flag i of every XCD copy of a flag array (lanes 0..NREP-1, one each).
+__device__ __forceinline__ void raise_flag(uint32_t* ctrl, int page_off, int i) {
+  const int l = lane_id();
+  if (l < NREP) store_agent(&ctrl[PAGE0 + l * PAGE_WORDS + page_off + i], 1u);
 }
 
-// Fill the B-operand pointers of stream nb for weight n-tile jn of a packed
-// [N, Kd] weight.
-template <class S, int FMT>
-__device__ __forceinline__ void set_b(S& st, int nb, const uint8_t* codes, const void* scales, int jn,
-                                      int Kd, int kt0) {
-  const int l = threadIdx.x & 63;
-  const int KT = Kd >> 7, KG = (KT + 3) >> 2;
-  st.bshared[nb] = codes + ((size_t)jn * KT + kt0) * 2048;
-  st.bt[nb] = st.bshared[nb] + l * 16;
-  if (FMT == FMT_BLOCK)
-    st.bsf[nb] = static_cast<const float*>(scales) + (size_t)(jn >> 3) * KT;
-  else
-    st.bsm[nb] = static_cast<const uint32_t*>(scales) + (size_t)jn * KG * 64 + l;
+// Spin until flags [0, n) of this XCD's copy are all set.
+__device__ __forceinline__ void wait_flags(const uint32_t* flags, int n) {
+  const int l = lane_id();
+  for (;;) {
+    bool ok = true;
+    for (int i = l; i < n; i += 64) ok = ok && load_agent(flags + i) != 0u;
+    if (__all(ok)) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Write this wavefront's accumulators to LDS (waves 1..3); wave 0 keeps its
-// own in registers and adds the others after the barrier.
-template <int NB, int MT>
-__device__ __forceinline__ void reduce_to_wave0(v4f (&acc)[NB][MT], v4f* red) {
-  const int w = wave_id(), l = threadIdx.x & 63;
-  if (w > 0) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) red[(((w - 1) * NB + nb) * MT + mt) * 64 + l] = acc[nb][mt];
+// Sum of the split-K partials of a shared band over its workgroups, in
+// workgroup order.  part: [G][2][2][M][16]; returns element (nb, row, col).
+__device__ __forceinline__ float sum_shared(const Args& a, const Phase& ph, const float* part, int b, int nb,
+                                            int row, int col) {
+  const int w0 = owner_wg(ph, b * ph.CPB), w1 = owner_wg(ph, b * ph.CPB + ph.CPB - 1);
+  float v = 0.0f;
+  for (int w = w0; w <= w1; ++w) {
+    const int side = band_side(ph, w, b);
+    v += ld_coherent(part + ((((size_t)w * 2 + side) * 2 + nb) * a.M + row) * 16 + col);
   }
-  __syncthreads();
-  if (w == 0) {
-#pragma unroll
-    for (int ww = 0; ww < NW - 1; ++ww)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] += red[((ww * NB + nb) * MT + mt) * 64 + l];
-  }
+  return v;
 }
 
-// ---------------------------------------------------------------------------
-// GU item j: 16 ffn columns, gate and up over all of d.
-// ---------------------------------------------------------------------------
-template <int MT, int FMT>
-__device__ void item_gu(const StreamArgs& a, int j, v4f* red, WgState& ws) {
-  const int w = wave_id(), l = threadIdx.x & 63;
-  const int KT = a.K1 >> 7;
-  const int KTw = (KT + NW - 1) / NW;
-  const int kt0 = min(KT, w * KTw);
-  const int nk = min(KT, kt0 + KTw) - kt0;
-  StreamerBf16<MT, 2, FMT, DepthBf16<MT>::P> st;
-  st.kt0 = kt0;
-  st.nk = nk;
-  {
-    const int KG = (KT + 3) >> 2;
-    const uint8_t* wc[2] = {a.wg, a.wu};
-    const void* wsc[2] = {a.sg, a.su};
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      st.bshared[nb] = wc[nb] + ((size_t)j * KT + kt0) * 2048;
-      st.bt[nb] = st.bshared[nb] + l * 16;
-      if (FMT == FMT_BLOCK) {
-        st.bsf[nb] = static_cast<const float*>(wsc[nb]) + (size_t)(j >> 3) * KT;
-      } else {
-        const uint32_t* base = static_cast<const uint32_t*>(wsc[nb]) + (size_t)j * KG * 64 + (l & 15);
-        st.bsm0[nb] = base + 16 * ((l >> 4) >> 1);
-        st.bsm1[nb] = base + 16 * (2 + ((l >> 4) >> 1));
-      }
-    }
-    st.arow = a.xb + (size_t)(l & 15) * a.K1 + 16 * (l >> 4);
-    st.ashared = a.xb + (size_t)kt0 * 128;
-    st.a_mt_stride = (size_t)16 * a.K1;
-    st.Mpad = a.Mpad;
-    if (FMT == FMT_BLOCK) st.asf = static_cast<const float*>(a.xs) + 4 * (l >> 4);
-  }
-  v4f acc[2][MT];
+// Store this workgroup's sums of shared band b and arrive; true if this was
+// the last workgroup of the band (all partials are then visible).
+template <int MT>
+__device__ __forceinline__ bool arrive_shared(const Args& a, const Phase& ph, float* part, uint32_t* cnt, int b,
+                                              const v4f (&s)[2][MT], int nsh) {
+  const int l = lane_id();
+  const int side = band_side(ph, blockIdx.x, b);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
-  const uint32_t* xq_done = &a.ctrl[C_XQ];
-  const uint32_t n_xq = (uint32_t)a.n_xq;
-  st.run(
-      acc, [&]() { return uniform(*(volatile uint32_t*)&ws.xq_seen) != 0; },
-      [&]() {
-        wait_geq(xq_done, n_xq);
-        ws.xq_seen = 1;
-      });
-  reduce_to_wave0<2, MT>(acc, red);
-  if (w == 0) {
-#pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = mt * 16 + 4 * (l >> 4) + r;
-        if (row < a.M) {
-          const float g = acc[0][mt][r], u = acc[1][mt][r];
-          st_coherent(a.a32 + (size_t)row * a.F + j * 16 + (l & 15), g / (1.0f + expf(-g)) * u);
-        }
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = mt * 16 + 4 * (l >> 4) + rr;
+        if (row < a.M)
+          st_coherent(part + ((((size_t)blockIdx.x * 2 + side) * 2 + nb) * a.M + row) * 16 + (l & 15), s[nb][mt][rr]);
       }
-    drain_memory();
-  }
-  __syncthreads();
-  const int grp = j >> 3;
-  if (threadIdx.x == 0) ws.flag = (atomic_add_agent(&a.ctrl[a.off_grp + grp], 1) == 7u);
-  __syncthreads();
-  if (ws.flag) {
-    requant_group<FMT>(a, grp);
-    drain_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      store_agent(&a.ctrl[a.off_grp + grp], 0u);
-      store_agent(&a.ctrl[a.off_ready + grp], 1u);
+  drain_memory();
+  uint32_t old = 0;
+  if (l == 0) old = atomic_add_agent(cnt + b, 1u);
+  const bool last = uni((int)old) == nsh - 1;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return last;
+}
+
+template <int MT, int NS, int NSLOT>
+__device__ __forceinline__ void take_event(Lds<MT, NS, NSLOT>& L, int k, v4f (&s)[2][MT]) {
+  const int slot = k % NSLOT;
+  lds_wait_geq(&L.arrived[slot], (uint32_t)NS);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v4f v = L.part[slot][0][nb][mt][lane_id()];
+#pragma unroll
+      for (int w = 1; w < NS; ++w) v += L.part[slot][w][nb][mt][lane_id()];
+      s[nb][mt] = v;
     }
+  if (lane_id() == 0) {
+    lds_store(&L.arrived[slot], 0u);
+    lds_store(&L.consumed, (uint32_t)(k + 1));
   }
 }
 
-// ---------------------------------------------------------------------------
-// DN item: NTD*16 output columns x one K chunk of the second GEMM.
-// ---------------------------------------------------------------------------
 template <int MT, int FMT>
-__device__ void item_dn(const StreamArgs& a, int i, v4f* red, WgState& ws) {
-  const int w = wave_id(), l = threadIdx.x & 63;
-  const int kc = i / a.n_dt, dt = i % a.n_dt;
-  const int KT2 = a.K2 >> 7;
-  const int kbeg = kc * a.ktc, kend = min(KT2, kbeg + a.ktc);
-  const int KTw = (kend - kbeg + NW - 1) / NW;
-  const int kt0 = min(kend, kbeg + w * KTw);
-  const int nk = min(kend, kt0 + KTw) - kt0;
-  Streamer<MT, NTD, FMT, Depth<MT>::P> st;
-  st.kt0 = kt0;
-  st.nk = nk;
+__device__ __forceinline__ void finish_gu_band(const Args& a, int b, v4f (&s)[2][MT]) {
+  const int l = lane_id();
+  const Phase& ph = a.gu;
+  const int nsh = owner_wg(ph, b * ph.CPB + ph.CPB - 1) - owner_wg(ph, b * ph.CPB) + 1;
+  if (nsh > 1) {
+    if (!arrive_shared<MT>(a, ph, a.gpart, a.ctrl + C_GPCNT, b, s, nsh)) return;
 #pragma unroll
-  for (int s = 0; s < NTD; ++s) set_b<decltype(st), FMT>(st, s, a.w2, a.s2, dt * NTD + s, a.K2, kt0);
-  if (a.mlp)
-    set_a<decltype(st), FMT>(st, a.aq, a.as, a.F, a.Mpad, kt0);
-  else
-    set_a<decltype(st), FMT>(st, a.xq, a.xs, a.K1, a.Mpad, kt0);
-  v4f acc[NTD][MT];
-#pragma unroll
-  for (int nb = 0; nb < NTD; ++nb)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (a.mlp) {
-    const uint32_t* ready = &a.ctrl[a.off_ready];
-    auto seen = [&](int g) { return (uniform(*(volatile uint32_t*)&ws.grp_seen[g >> 5]) >> (g & 31)) & 1u; };
-    st.run(
-        acc,
-        [&]() {
-          bool ok = true;
-          for (int kt = kt0; kt < kt0 + nk; ++kt) ok = ok && seen(kt);
-          return ok;
-        },
-        [&]() {
-          for (int kt = kt0; kt < kt0 + nk; ++kt) {
-            if (!seen(kt)) {
-              wait_geq(&ready[kt], 1u);
-              if ((threadIdx.x & 63) == 0) atomicOr(&ws.grp_seen[kt >> 5], 1u << (kt & 31));
-            }
-          }
-        });
-  } else {
-    const uint32_t* xq_done = &a.ctrl[C_XQ];
-    const uint32_t n_xq = (uint32_t)a.n_xq;
-    st.run(
-        acc, [&]() { return uniform(*(volatile uint32_t*)&ws.xq_seen) != 0; },
-        [&]() {
-          wait_geq(xq_done, n_xq);
-          ws.xq_seen = 1;
-        });
-  }
-  reduce_to_wave0<NTD, MT>(acc, red);
-  if (w == 0) {
-#pragma unroll
-    for (int s = 0; s < NTD; ++s)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = mt * 16 + 4 * (l >> 4) + r;
-          const int col = (dt * NTD + s) * 16 + (l & 15);
-          if (row < a.M) {
-            if (a.n_kc == 1)
-              a.y[(size_t)row * a.N + col] = (uint16_t)f32_to_bf16(acc[s][mt][r]);
-            else
-              st_coherent(a.ypart + ((size_t)kc * a.M + row) * a.N + col, acc[s][mt][r]);
-          }
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = mt * 16 + 4 * (l >> 4) + rr;
+          if (row < a.M) s[nb][mt][rr] = sum_shared(a, ph, a.gpart, b, nb, row, l & 15);
         }
-    if (a.n_kc > 1) drain_memory();
   }
-  if (a.n_kc == 1) return;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    ws.flag = (atomic_add_agent(&a.ctrl[a.off_ycnt + dt], 1) == (uint32_t)(a.n_kc - 1));
-  __syncthreads();
-  if (ws.flag) {
-    constexpr int COLS = NTD * 16;
-    for (int e = threadIdx.x; e < a.M * COLS; e += NW * 64) {
-      const int row = e / COLS, col = dt * COLS + e % COLS;
-      float v = 0.0f;
-      for (int c = 0; c < a.n_kc; ++c) v += ld_coherent(a.ypart + ((size_t)c * a.M + row) * a.N + col);
-      a.y[(size_t)row * a.N + col] = (uint16_t)f32_to_bf16(v);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = mt * 16 + 4 * (l >> 4) + rr;
+      if (row < a.M) st_coherent(a.a32 + (size_t)row * a.F + b * 16 + (l & 15), silu_mul(s[0][mt][rr], s[1][mt][rr]));
     }
-    if (threadIdx.x == 0) store_agent(&a.ctrl[a.off_ycnt + dt], 0u);
+  drain_memory();
+  const int grp = b >> 3;
+  uint32_t old = 0;
+  if (l == 0) old = atomic_add_agent(&a.ctrl[C_GCNT + grp], 1u);
+  if (uni((int)old) != 7) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  requant_group<FMT>(a, grp);
+  drain_memory();
+  raise_flag(a.ctrl, PG_RDY, grp);
+}
+
+template <int MT>
+__device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2][MT]) {
+  const int l = lane_id();
+  const Phase& ph = a.dn;
+  const int nsh = owner_wg(ph, b * ph.CPB + ph.CPB - 1) - owner_wg(ph, b * ph.CPB) + 1;
+  if (nsh > 1) {
+    if (!arrive_shared<MT>(a, ph, a.dpart, a.ctrl + C_DPCNT, b, s, nsh)) return;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = mt * 16 + 4 * (l >> 4) + rr;
+          if (row < a.M) s[nb][mt][rr] = sum_shared(a, ph, a.dpart, b, nb, row, l & 15);
+        }
   }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = mt * 16 + 4 * (l >> 4) + rr;
+        if (row < a.M) a.y[(size_t)row * a.N + b * 32 + nb * 16 + (l & 15)] = (uint16_t)f32_to_bf16(s[nb][mt][rr]);
+      }
+}
+
+template <int MT, int FMT, int NS, int NSLOT>
+__device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L) {
+  const int l = lane_id();
+  const int W = blockIdx.x;
+  const int rep = W & (NREP - 1);
+  const uint32_t* page = a.ctrl + PAGE0 + rep * PAGE_WORDS;
+  // quantize this workgroup's share of x, then wait for everyone's
+  if (W < a.n_items) {
+    xq_item<FMT>(a, W);
+    drain_memory();
+    raise_flag(a.ctrl, PG_XQ, W);
+  }
+  wait_flags(page + PG_XQ, a.n_items);
+  if (l == 0) lds_store(&L.xq_ok, 1u);
+
+  int k = 0;
+  if (a.mlp && W < a.gu.nwg) {
+    const Phase& ph = a.gu;
+    const int c0 = range_start(ph, W), c1 = range_start(ph, W + 1);
+    if (c0 < c1) {
+      for (int b = c0 / ph.CPB; b <= (c1 - 1) / ph.CPB; ++b) {
+        v4f s[2][MT];
+        take_event(L, k++, s);
+        finish_gu_band<MT, FMT>(a, b, s);
+      }
+    }
+  }
+  if (W < a.dn.nwg) {
+    const Phase& ph = a.dn;
+    const int c0 = range_start(ph, W), c1 = range_start(ph, W + 1);
+    if (c0 < c1) {
+      if (a.mlp) {
+        // groups (k-tiles of the second GEMM) this workgroup's chunks read
+        int g0 = 0, g1 = ph.KT;
+        if (c0 / ph.CPB == (c1 - 1) / ph.CPB) {
+          g0 = (c0 % ph.CPB) * Cfg<MT>::P;
+          g1 = min(ph.KT, ((c1 - 1) % ph.CPB) * Cfg<MT>::P + Cfg<MT>::P);
+        }
+        wait_flags(page + PG_RDY + g0, g1 - g0);
+        if (l == 0) lds_store(&L.dn_ok, 1u);
+      }
+      for (int b = c0 / ph.CPB; b <= (c1 - 1) / ph.CPB; ++b) {
+        v4f s[2][MT];
+        take_event(L, k++, s);
+        finish_dn_band<MT>(a, b, s);
+      }
+    }
+  }
+  // leave; the last workgroup clears the control block
+  drain_memory();
+  uint32_t old = 0;
+  if (l == 0) old = atomic_add_agent(&a.ctrl[C_DONE], 1u);
+  if (uni((int)old) != a.G - 1) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  for (int i = l; i < a.n_items; i += 64)
+    for (int r = 0; r < NREP; ++r) store_agent(&a.ctrl[PAGE0 + r * PAGE_WORDS + PG_XQ + i], 0u);
+  for (int i = l; i < a.ngroups; i += 64) {
+    for (int r = 0; r < NREP; ++r) store_agent(&a.ctrl[PAGE0 + r * PAGE_WORDS + PG_RDY + i], 0u);
+    store_agent(&a.ctrl[C_GCNT + i], 0u);
+  }
+  if (a.mlp)
+    for (int i = l; i < a.gu.nbands; i += 64) store_agent(&a.ctrl[C_GPCNT + i], 0u);
+  for (int i = l; i < a.dn.nbands; i += 64) store_agent(&a.ctrl[C_DPCNT + i], 0u);
+  if (l == 0) store_agent(&a.ctrl[C_DONE], 0u);
 }
 
 // ---------------------------------------------------------------------------
-// The persistent kernel.
+// The persistent kernel: wavefront 0 syncs, the others stream.
 // ---------------------------------------------------------------------------
 template <int MT, int FMT>
-__global__ __launch_bounds__(NW * 64, (MT >= 8 ? 1 : 2)) void stream_kernel(StreamArgs a) {
-  __shared__ v4f red[(NW - 1) * 2 * MT * 64];
-  __shared__ WgState ws;
+__global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) {
+  using C = Cfg<MT>;
+  __shared__ Lds<MT, C::NS, C::NSLOT> L;
+  const int wv = uni((int)(threadIdx.x >> 6));
   if (threadIdx.x == 0) {
-    ws.xq_seen = 0;
-    for (int k = 0; k < 8; ++k) ws.grp_seen[k] = 0;
+    for (int i = 0; i < C::NSLOT; ++i) L.arrived[i] = 0u;
+    L.consumed = 0u;
+    L.xq_ok = 0u;
+    L.dn_ok = 0u;
   }
   __syncthreads();
-  int ticket = blockIdx.x;
-  while (ticket < a.total) {
-    // take the next ticket now; its latency overlaps this item
-    uint32_t next = 0;
-    if (threadIdx.x == 0) next = gridDim.x + atomic_add_agent(&a.ctrl[C_TICKET], 1);
-    if (ticket < a.n_xq)
-      item_xq<FMT>(a, ticket);
-    else if (ticket < a.n_xq + a.n_gu)
-      item_gu<MT, FMT>(a, ticket - a.n_xq, red, ws);
-    else
-      item_dn<MT, FMT>(a, ticket - a.n_xq - a.n_gu, red, ws);
-    __syncthreads();
-    if (threadIdx.x == 0) ws.ticket = next;
-    __syncthreads();
-    ticket = (int)uniform(ws.ticket);
-  }
-  if (threadIdx.x == 0) {
-    if (atomic_add_agent(&a.ctrl[C_DONE], 1) == gridDim.x - 1) {
-      // Every workgroup has taken its last ticket: reset the control block.
-      const int n = a.off_ycnt + a.n_dt;
-      for (int k = C_HDR; k < n; ++k) store_agent(&a.ctrl[k], 0u);
-      store_agent(&a.ctrl[C_XQ], 0u);
-      store_agent(&a.ctrl[C_TICKET], 0u);
-      store_agent(&a.ctrl[C_DONE], 0u);
-    }
+  if (wv == 0) {
+    sync_wave<MT, FMT>(a, L);
+  } else {
+    Streamer<MT, FMT, C::P> st(a, wv - 1);
+    int k = 0;
+    if (a.mlp) st.template run_phase<true>(L, k);
+    st.template run_phase<false>(L, k);
   }
 }
 
@@ -701,57 +753,59 @@ __global__ __launch_bounds__(NW * 64, (MT >= 8 ? 1 : 2)) void stream_kernel(Stre
 namespace {
 
 struct Plan {
-  int MT, Mpad;
-  int n_xq, n_gu, n_dt, n_kc, ktc, total;
-  int off_grp, off_ready, off_ycnt, ctrl_words;
-  size_t off_xq, off_xs, off_a32, off_aq, off_as, off_ypart, bytes;  // off_xq: xq (GEMM) or xb (MLP)
+  int ok;
+  int MT, Mpad, G, n_pairs, n_items, ngroups;
+  Phase gu, dn;
+  size_t off_xa, off_xs, off_a32, off_aq, off_as, off_gpart, off_dpart, bytes;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-
 int mt_for(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
+int cfg_ns(int MT) { return MT == 1 ? Cfg<1>::NS : MT == 2 ? Cfg<2>::NS : MT == 4 ? Cfg<4>::NS : Cfg<8>::NS; }
+int cfg_p(int MT) { return MT == 1 ? Cfg<1>::P : MT == 2 ? Cfg<2>::P : MT == 4 ? Cfg<4>::P : Cfg<8>::P; }
+int cfg_nwave(int MT) { return cfg_ns(MT) + 1; }
 
-Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp) {
+Phase make_phase(int KT, int nbands, int P, int NS, int G) {
+  Phase ph{};
+  ph.KT = KT;
+  ph.CPB = (KT + P - 1) / P;
+  ph.nbands = nbands;
+  ph.nchunks = nbands * ph.CPB;
+  const int nwg = ph.nchunks / NS;
+  ph.nwg = nwg < 1 ? 1 : (nwg > G ? G : nwg);
+  return ph;
+}
+
+Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp, int G) {
   Plan p{};
   p.MT = mt_for(M);
   p.Mpad = 16 * p.MT;
-  p.n_xq = (p.Mpad * (K1 / 128) + XQ_GPI - 1) / XQ_GPI;
-  p.n_gu = mlp ? F / 16 : 0;
-  p.n_dt = N / (16 * NTD);
-  const int KT2 = K2 / 128;
-  // K chunk of a DN item: about as many weight bytes as a GU item
-  // (2 * 16 * d), and at least 4 k-tiles per chunk.
-  int ktc = mlp ? K1 / 128 : KT2;
-  if (!mlp) {
-    // plain GEMM: split K so that there are enough items to fill the chip
-    const int want_items = 1024;
-    int chunks = (want_items + p.n_dt - 1) / p.n_dt;
-    if (chunks > KT2 / 4) chunks = KT2 / 4 > 0 ? KT2 / 4 : 1;
-    ktc = (KT2 + chunks - 1) / chunks;
-  }
-  if (ktc < 4) ktc = 4;
-  if (ktc > KT2) ktc = KT2;
-  p.ktc = ktc;
-  p.n_kc = (KT2 + ktc - 1) / ktc;
-  p.total = p.n_xq + p.n_gu + p.n_dt * p.n_kc;
-  const int ng = mlp ? F / 128 : 0;
-  p.off_grp = C_HDR;
-  p.off_ready = p.off_grp + ng;
-  p.off_ycnt = p.off_ready + ng;
-  p.ctrl_words = p.off_ycnt + p.n_dt;
-  size_t o = align256((size_t)p.ctrl_words * 4);
-  p.off_xq = o;
-  o = align256(o + (size_t)p.Mpad * K1 * (mlp ? 2 : 1));
+  p.G = G;
+  const int P = cfg_p(p.MT), NS = cfg_ns(p.MT);
+  const int KT1 = K1 / 128;
+  p.n_pairs = KT1 * p.MT;
+  p.n_items = p.n_pairs < G ? p.n_pairs : G;
+  if (p.n_items > MAX_ITEMS) p.n_items = MAX_ITEMS;
+  p.ngroups = mlp ? F / 128 : 0;
+  if (mlp) p.gu = make_phase(KT1, F / 16, P, NS, G);
+  p.dn = make_phase(K2 / 128, N / 32, P, NS, G);
+  p.ok = p.ngroups <= MAX_GROUPS && (!mlp || F / 16 <= MAX_GBANDS) && N / 32 <= CTRL_WORDS - C_DPCNT;
+  size_t o = CTRL_BYTES;
+  p.off_xa = o;
+  o = align256(o + (size_t)M * K1);
   p.off_xs = o;
-  o = align256(o + (fmt == FMT_BLOCK ? (size_t)(K1 / 128) * p.Mpad * 4 : (size_t)p.Mpad * (K1 / 32)));
+  o = align256(o + (fmt == FMT_BLOCK ? (size_t)KT1 * p.Mpad * 4 : (size_t)M * (K1 / 32)));
+  const size_t part = (size_t)MAX_WG * 2 * 2 * M * 16 * 4;
   p.off_a32 = o;
   if (mlp) o = align256(o + (size_t)M * F * 4);
   p.off_aq = o;
-  if (mlp) o = align256(o + (size_t)p.Mpad * F);
+  if (mlp) o = align256(o + (size_t)M * F);
   p.off_as = o;
-  if (mlp) o = align256(o + (fmt == FMT_BLOCK ? (size_t)(F / 128) * p.Mpad * 4 : (size_t)p.Mpad * (F / 32)));
-  p.off_ypart = o;
-  if (p.n_kc > 1) o = align256(o + (size_t)p.n_kc * M * N * 4);
+  if (mlp) o = align256(o + (fmt == FMT_BLOCK ? (size_t)(F / 128) * p.Mpad * 4 : (size_t)M * (F / 32)));
+  p.off_gpart = o;
+  if (mlp) o = align256(o + part);
+  p.off_dpart = o;
+  o = align256(o + part);
   p.bytes = o;
   return p;
 }
@@ -776,7 +830,9 @@ const void* pick_kernel(int MT, int fmt) {
   }
 }
 
-// Resident workgroups per device for each kernel variant (queried once).
+// Workgroups resident at once on the current device for each kernel variant
+// (queried once per device): the grid, so that every workgroup runs
+// concurrently with every other.
 struct Occupancy {
   std::mutex mu;
   int cus[64] = {0};
@@ -784,7 +840,7 @@ struct Occupancy {
 };
 Occupancy g_occ;
 
-int resident_blocks(const void* kern, int MT, int fmt, int* out) {
+int grid_size(int MT, int fmt, int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SGD_EHIP;
   const int fi = fmt == FMT_BLOCK ? 0 : 1;
@@ -798,7 +854,9 @@ int resident_blocks(const void* kern, int MT, int fmt, int* out) {
   }
   if (g_occ.per_cu[dev][fi][mi] == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, NW * 64, 0) != hipSuccess || nb <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, pick_kernel(MT, fmt), 64 * cfg_nwave(MT), 0) !=
+            hipSuccess ||
+        nb <= 0)
       return SGD_EHIP;
     g_occ.per_cu[dev][fi][mi] = nb;
   }
@@ -809,14 +867,21 @@ int resident_blocks(const void* kern, int MT, int fmt, int* out) {
 }  // namespace
 
 size_t stream_workspace_bytes(int fmt, int M, int K1, int F, int N, int K2, bool mlp) {
-  return make_plan(fmt, M, K1, F, N, K2, mlp).bytes;
+  // the layout does not depend on the grid (partial slots are sized for MAX_WG)
+  const Plan p = make_plan(fmt, M, K1, F, N, K2, mlp, MAX_WG);
+  return p.ok ? p.bytes : 0;
 }
 
 int launch_stream(const Problem& pr, hipStream_t s) {
   const bool mlp = pr.gate != nullptr;
   const int F = mlp ? pr.gate->N : 0;
-  const Plan p = make_plan(pr.fmt, pr.M, pr.K1, F, pr.w2->N, pr.w2->K, mlp);
-  StreamArgs a{};
+  int G = 0;
+  int rc = grid_size(mt_for(pr.M), pr.fmt, &G);
+  if (rc != SGD_OK) return rc;
+  if (G > MAX_WG) G = MAX_WG;
+  const Plan p = make_plan(pr.fmt, pr.M, pr.K1, F, pr.w2->N, pr.w2->K, mlp, G);
+  if (!p.ok) return SGD_EDIM;
+  Args a{};
   a.M = pr.M;
   a.Mpad = p.Mpad;
   a.mlp = mlp ? 1 : 0;
@@ -827,43 +892,32 @@ int launch_stream(const Problem& pr, hipStream_t s) {
     a.sg = pr.gate->scales;
     a.wu = static_cast<const uint8_t*>(pr.up->codes);
     a.su = pr.up->scales;
+    a.scale_bytes_g = (uint32_t)sgd_packed_scales_bytes(pr.fmt, F, pr.K1);
   }
   a.F = F;
   a.w2 = static_cast<const uint8_t*>(pr.w2->codes);
   a.s2 = pr.w2->scales;
   a.N = pr.w2->N;
   a.K2 = pr.w2->K;
+  a.scale_bytes_2 = (uint32_t)sgd_packed_scales_bytes(pr.fmt, a.N, a.K2);
   a.y = pr.y;
   uint8_t* ws = static_cast<uint8_t*>(pr.ws);
   a.ctrl = reinterpret_cast<uint32_t*>(ws);
-  a.xq = ws + p.off_xq;
-  a.xb = reinterpret_cast<uint16_t*>(ws + p.off_xq);
+  a.xa = ws + p.off_xa;
   a.xs = ws + p.off_xs;
   a.a32 = reinterpret_cast<float*>(ws + p.off_a32);
   a.aq = ws + p.off_aq;
   a.as = ws + p.off_as;
-  a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
-  a.n_xq = p.n_xq;
-  a.n_gu = p.n_gu;
-  a.n_dt = p.n_dt;
-  a.n_kc = p.n_kc;
-  a.ktc = p.ktc;
-  a.total = p.total;
-  a.off_grp = p.off_grp;
-  a.off_ready = p.off_ready;
-  a.off_ycnt = p.off_ycnt;
-
-  const void* kern = pick_kernel(p.MT, pr.fmt);
-  int resident = 0;
-  int rc = resident_blocks(kern, p.MT, pr.fmt, &resident);
-  if (rc != SGD_OK) return rc;
-  // Workgroups are dispatched in index order, so the first (static) tickets
-  // and every later (atomic) ticket reach workgroups that are already
-  // running: a wait only ever targets an item that is being worked on.
-  int grid = resident < p.total ? resident : p.total;
-  if (grid < 1) grid = 1;
+  a.gpart = reinterpret_cast<float*>(ws + p.off_gpart);
+  a.dpart = reinterpret_cast<float*>(ws + p.off_dpart);
+  a.G = G;
+  a.n_pairs = p.n_pairs;
+  a.n_items = p.n_items;
+  a.ngroups = p.ngroups;
+  a.gu = p.gu;
+  a.dn = p.dn;
   void* args[] = {&a};
-  return hip_status(hipLaunchKernel(kern, dim3(grid), dim3(NW * 64), args, 0, s));
+  return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, 0, s));
 }
 
 }  // namespace sgd
