@@ -172,6 +172,9 @@ __device__ __forceinline__ float ld_coherent(const float* p) {
   return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT));
 }
+__device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Wait until every memory operation this wavefront issued has completed.
 __device__ __forceinline__ void drain_memory() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

@@ -55,7 +55,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 template <int MT>
 struct Cfg {
   static constexpr int NS = MT >= 4 ? 3 : 7;
-  static constexpr int P = MT >= 8 ? 2 : 4;
+  static constexpr int P = (MT == 2 || MT >= 8) ? 2 : 4;
   static constexpr int NSLOT = 2;
   static constexpr int NWAVE = NS + 1;
 };
@@ -174,10 +174,28 @@ __device__ __forceinline__ void lds_wait_geq(const uint32_t* p, uint32_t target)
 // ---------------------------------------------------------------------------
 // Streaming wavefront
 // ---------------------------------------------------------------------------
-template <int MT, int FMT, int P>
+// Where a phase's chunk walk stands.
+struct PhaseState {
+  int active;     // this workgroup has chunks in the phase
+  int c, c1;      // this wavefront's next chunk; end of the workgroup's range
+  int bf, bl;     // first and last band of the range
+  ChunkPos cp;    // position of chunk c
+};
+
+// LDS copy of Q(x) (used when it fits): codes [Mpad][K1 + 16] (rows padded
+// by 16 bytes so the 16 rows of an operand load fall in distinct banks), then
+// the scales: block fp32 [K1/128][Mpad]; mx E8M0 [Mpad][K1/32].
+__host__ __device__ constexpr int xl_row_stride(int K1) { return K1 + 16; }
+__host__ __device__ constexpr int xl_scale_offset(int Mpad, int K1) { return Mpad * (K1 + 16); }
+__host__ __device__ constexpr int xl_bytes(int fmt, int Mpad, int K1) {
+  return xl_scale_offset(Mpad, K1) + (fmt == FMT_BLOCK ? (K1 / 128) * Mpad * 4 : Mpad * (K1 / 32));
+}
+
+template <int MT, int FMT, int P, int XL>
 struct Streamer {
   const Args& a;
   const int q;  // index among the workgroup's streaming wavefronts
+  const uint8_t* lx;  // LDS copy of Q(x) (XL)
   // ring: weights of stream 0/1 and their scale words (block: fp32 bits in
   // S0; mx: S0/S1 = dwords holding this lane's two 32-column-block scales for
   // gate/up, its own scale slot for the second GEMM), fp8 activations (one
@@ -198,7 +216,7 @@ struct Streamer {
   uint32_t xs_lane, as_lane;       // activation-scale lane offsets (bytes)
   int KdA;                         // row length of the second GEMM's activation
 
-  __device__ Streamer(const Args& args, int wq) : a(args), q(wq) {
+  __device__ Streamer(const Args& args, int wq, const uint8_t* lds_x) : a(args), q(wq), lx(lds_x) {
     const int l = lane_id();
     lo16 = (uint32_t)l * 16u;
     mo_gu0 = ((uint32_t)(l & 15) + 16u * (uint32_t)((l >> 4) >> 1)) * 4u;
@@ -287,6 +305,29 @@ struct Streamer {
     const bool ok = cp.ok && kt_ < KT;
     const uint32_t kt = ok ? (uint32_t)kt_ : 0u;
     const uint32_t Kd = GU ? (uint32_t)a.K1 : (uint32_t)KdA;
+    if (XL && (GU || !a.mlp)) {
+      // Q(x) from LDS (fillers read k-tile 0 and are never used)
+      const int l = lane_id();
+      const int rs = xl_row_stride(a.K1);
+      const uint8_t* sc = lx + xl_scale_offset(16 * MT, a.K1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint8_t* p = lx + (mt * 16 + (l & 15)) * rs + kt * 128 + 16 * (l >> 4);
+        RA[s][mt] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+        if (FMT == FMT_BLOCK) {
+          XB[s][mt] = *reinterpret_cast<const v4f*>(sc + (kt * (16 * MT) + 16 * mt + 4 * (l >> 4)) * 4);
+        } else {
+          const uint8_t* e = sc + (mt * 16 + (l & 15)) * (a.K1 >> 5) + 4 * kt;
+          if (GU) {
+            X0[s][mt] = e[(l >> 4) >> 1];
+            X1[s][mt] = e[2 + ((l >> 4) >> 1)];
+          } else {
+            X0[s][mt] = e[l >> 4];
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint32_t o = ok ? (GU ? xa_lane : aq_lane) + (uint32_t)mt * 16u * Kd + kt * 128u : OOB;
@@ -396,26 +437,40 @@ struct Streamer {
       __hip_atomic_fetch_add(&L.arrived[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 
-  // Stream this workgroup's chunks of one phase.
-  template <bool GU, int NS, int NSLOT>
-  __device__ __forceinline__ void run_phase(Lds<MT, NS, NSLOT>& L, int& k) {
+  // Start a phase: find this workgroup's chunks and fill the ring with the
+  // weights of this wavefront's first chunk.
+  template <bool GU>
+  __device__ __forceinline__ void begin(PhaseState& st) {
     const Phase& ph = GU ? a.gu : a.dn;
     const int W = blockIdx.x;
+    st.active = 0;
     if (W >= ph.nwg) return;
-    const int c0 = range_start(ph, W), c1 = range_start(ph, W + 1);
-    if (c0 >= c1) return;
-    const int KT = ph.KT;
+    const int c0 = range_start(ph, W);
+    st.c1 = range_start(ph, W + 1);
+    if (c0 >= st.c1) return;
+    st.active = 1;
+    st.c = c0 + q;
+    st.bf = c0 / ph.CPB;
+    st.bl = (st.c1 - 1) / ph.CPB;
     make_resources(GU);
-    int c = c0 + q;
-    ChunkPos cp = chunk_pos<P>(ph, c, c1);
+    st.cp = chunk_pos<P>(ph, st.c, st.c1);
 #pragma unroll
-    for (int s = 0; s < P; ++s) load_b<GU>(s, cp, KT, s);
-    // activations only once they exist
-    lds_wait_geq(GU || !a.mlp ? &L.xq_ok : &L.dn_ok, 1u);
+    for (int s = 0; s < P; ++s) load_b<GU>(s, st.cp, ph.KT, s);
+  }
+
+  // Stream the rest of the phase.
+  template <bool GU, int NS, int NSLOT>
+  __device__ __forceinline__ void body(PhaseState& st, Lds<MT, NS, NSLOT>& L, int& k) {
+    if (!st.active) return;
+    const Phase& ph = GU ? a.gu : a.dn;
+    const int KT = ph.KT, c1 = st.c1;
+    int c = st.c;
+    ChunkPos cp = st.cp;
+    // activations only once they exist (the LDS copy of Q(x) already does)
+    if (!(XL && (GU || !a.mlp))) lds_wait_geq(GU || !a.mlp ? &L.xq_ok : &L.dn_ok, 1u);
 #pragma unroll
     for (int s = 0; s < P; ++s) load_a<GU>(s, cp, KT, s);
-    const int bf = c0 / ph.CPB, bl = (c1 - 1) / ph.CPB;
-    for (int b = bf; b <= bl; ++b) {
+    for (int b = st.bf; b <= st.bl; ++b) {
       const int hi = min(c1, (b + 1) * ph.CPB);
       v4f acc[2][MT];
 #pragma unroll
@@ -472,6 +527,110 @@ __device__ __forceinline__ void zero_pad_scales(float* col_of_group, int M, int 
   if (l + 64 >= M && l + 64 < Mpad) st_coherent(col_of_group + l + 64, 0.0f);
 }
 
+// All wavefronts of a workgroup quantize x into LDS (layout above): one lane
+// per (row, 32-column block).  The loads of a lane's first four blocks are
+// issued before the wavefront's first weight loads, so waiting for them does
+// not wait for the weights (the load counter completes in issue order).
+// E4M3 conversion in hardware after clamping to +-448 (round to nearest
+// even, checked against the integer encoder over 6.8e8 fp32 patterns on
+// gfx950).  Rows M..Mpad-1 become zero codes with zero scales.
+template <int FMT>
+struct XqLocal {
+  static constexpr int U = 4;  // blocks per lane whose loads go first
+  uint4 raw[U][4];
+
+  __device__ __forceinline__ void load(const Args& a) {
+    const int nb = a.K1 >> 5, T = a.M * nb;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (int)threadIdx.x + u * (int)blockDim.x;
+      if (i < T) {
+        const int r = i / nb, j = i - r * nb;
+        const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)r * a.K1 + 32 * j);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) raw[u][c] = src[c];
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void quant_block(const Args& a, uint8_t* lx, int Mpad, int i,
+                                                     const uint4 (&w)[4]) {
+    const int nb = a.K1 >> 5;
+    const int r = i / nb, j = i - r * nb;
+    uint8_t* sc = lx + xl_scale_offset(Mpad, a.K1);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * c + 2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
+        v[8 * c + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+      }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(v[e]));
+    float mul = 1.0f, sf = 1.0f;
+    if (FMT == FMT_BLOCK) {
+      // the 4 blocks of a 128-column group sit in 4 consecutive lanes
+      am = fmaxf(am, __shfl_xor(am, 1, WAVE));
+      am = fmaxf(am, __shfl_xor(am, 2, WAVE));
+      sf = block_scale(am);
+      if ((j & 3) == 0) reinterpret_cast<float*>(sc)[(j >> 2) * Mpad + r] = sf;
+    } else {
+      const int X = mx_exponent(am);
+      mul = pow2_neg(X);
+      sc[r * nb + j] = (uint8_t)(X + 127);
+    }
+    uint32_t cw[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = FMT == FMT_BLOCK ? v[4 * c + e] / sf : v[4 * c + e] * mul;
+        q[e] = __builtin_amdgcn_fmed3f(t, -E4M3_MAX, E4M3_MAX);
+      }
+      int wv = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      wv = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], wv, true);
+      cw[c] = (uint32_t)wv;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(lx + r * xl_row_stride(a.K1) + 32 * j);
+    dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    dst[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+  }
+
+  __device__ __forceinline__ void finish(const Args& a, uint8_t* lx, int Mpad) {
+    const int nb = a.K1 >> 5, T = a.M * nb, nt = blockDim.x, t = threadIdx.x;
+    // (T is a multiple of 4, so the 4 lanes of a block group agree on i < T)
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t + u * nt < T) quant_block(a, lx, Mpad, t + u * nt, raw[u]);
+    for (int i = t + U * nt; i < T; i += nt) {
+      const int r = i / nb, j = i - r * nb;
+      const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)r * a.K1 + 32 * j);
+      uint4 w[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = src[c];
+      quant_block(a, lx, Mpad, i, w);
+    }
+    // padded rows
+    const int rs = xl_row_stride(a.K1);
+    const int nz = (Mpad - a.M) * rs / 16;
+    uint4* z = reinterpret_cast<uint4*>(lx + a.M * rs);
+    for (int e = t; e < nz; e += nt) z[e] = make_uint4(0u, 0u, 0u, 0u);
+    uint8_t* sc = lx + xl_scale_offset(Mpad, a.K1);
+    if (FMT == FMT_BLOCK) {
+      const int pad = Mpad - a.M;
+      for (int e = t; e < (a.K1 >> 7) * pad; e += nt)
+        reinterpret_cast<float*>(sc)[(e / pad) * Mpad + a.M + e % pad] = 0.0f;
+    } else {
+      for (int e = t; e < (Mpad - a.M) * nb; e += nt) sc[a.M * nb + e] = 0u;
+    }
+  }
+};
+
 // Quantize x for one item: its (128-column group, 16-row tile) pairs.
 template <int FMT>
 __device__ __forceinline__ void xq_item(const Args& a, int item) {
@@ -502,16 +661,28 @@ __device__ __forceinline__ void xq_item(const Args& a, int item) {
   }
 }
 
+// Re-quantize 128-column group g of a = silu(g)*u, 16 rows per batch (all
+// loads of a batch are in flight together).
 template <int FMT>
 __device__ __forceinline__ void requant_group(const Args& a, int g) {
-  for (int row = 0; row < a.M; ++row) {
-    const float* src = a.a32 + (size_t)row * a.F + g * 128 + 2 * lane_id();
-    float sf = 1.0f;
-    uint32_t se = 0;
-    const uint32_t c = quant_pair<FMT>(ld_coherent(src), ld_coherent(src + 1), &sf, &se);
-    store_group<FMT>(a.aq + (size_t)row * a.F + g * 128, c, sf, se,
-                     static_cast<float*>(a.as) + (size_t)g * a.Mpad + row,
-                     static_cast<uint8_t*>(a.as) + (size_t)row * (a.F >> 5) + 4 * g);
+  const int l = lane_id();
+  for (int r0 = 0; r0 < a.M; r0 += 16) {
+    uint64_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      v[i] = ld_coherent(reinterpret_cast<const uint64_t*>(a.a32 + (size_t)min(r0 + i, a.M - 1) * a.F + g * 128 + 2 * l));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = r0 + i;
+      if (row < a.M) {
+        float sf = 1.0f;
+        uint32_t se = 0;
+        const uint32_t c = quant_pair<FMT>(__uint_as_float((uint32_t)v[i]), __uint_as_float((uint32_t)(v[i] >> 32)), &sf, &se);
+        store_group<FMT>(a.aq + (size_t)row * a.F + g * 128, c, sf, se,
+                         static_cast<float*>(a.as) + (size_t)g * a.Mpad + row,
+                         static_cast<uint8_t*>(a.as) + (size_t)row * (a.F >> 5) + 4 * g);
+      }
+    }
   }
   if (FMT == FMT_BLOCK) zero_pad_scales(static_cast<float*>(a.as) + (size_t)g * a.Mpad, a.M, a.Mpad);
 }
@@ -537,16 +708,29 @@ __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n) {
 }
 
 // Sum of the split-K partials of a shared band over its workgroups, in
-// workgroup order.  part: [G][2][2][M][16]; returns element (nb, row, col).
-__device__ __forceinline__ float sum_shared(const Args& a, const Phase& ph, const float* part, int b, int nb,
-                                            int row, int col) {
+// workgroup order (all of one workgroup's loads in flight together).
+// part: [G][2][2][M][16].
+template <int MT>
+__device__ __forceinline__ void sum_shared(const Args& a, const Phase& ph, const float* part, int b,
+                                           v4f (&s)[2][MT]) {
+  const int l = lane_id();
   const int w0 = owner_wg(ph, b * ph.CPB), w1 = owner_wg(ph, b * ph.CPB + ph.CPB - 1);
-  float v = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) s[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int w = w0; w <= w1; ++w) {
-    const int side = band_side(ph, w, b);
-    v += ld_coherent(part + ((((size_t)w * 2 + side) * 2 + nb) * a.M + row) * 16 + col);
+    const float* base = part + ((size_t)w * 2 + band_side(ph, w, b)) * 2 * a.M * 16;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = min(mt * 16 + 4 * (l >> 4) + rr, a.M - 1);
+          s[nb][mt][rr] += ld_coherent(base + ((size_t)nb * a.M + row) * 16 + (l & 15));
+        }
   }
-  return v;
 }
 
 // Store this workgroup's sums of shared band b and arrive; true if this was
@@ -600,15 +784,7 @@ __device__ __forceinline__ void finish_gu_band(const Args& a, int b, v4f (&s)[2]
   const int nsh = owner_wg(ph, b * ph.CPB + ph.CPB - 1) - owner_wg(ph, b * ph.CPB) + 1;
   if (nsh > 1) {
     if (!arrive_shared<MT>(a, ph, a.gpart, a.ctrl + C_GPCNT, b, s, nsh)) return;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = mt * 16 + 4 * (l >> 4) + rr;
-          if (row < a.M) s[nb][mt][rr] = sum_shared(a, ph, a.gpart, b, nb, row, l & 15);
-        }
+    sum_shared<MT>(a, ph, a.gpart, b, s);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -635,15 +811,7 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
   const int nsh = owner_wg(ph, b * ph.CPB + ph.CPB - 1) - owner_wg(ph, b * ph.CPB) + 1;
   if (nsh > 1) {
     if (!arrive_shared<MT>(a, ph, a.dpart, a.ctrl + C_DPCNT, b, s, nsh)) return;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = mt * 16 + 4 * (l >> 4) + rr;
-          if (row < a.M) s[nb][mt][rr] = sum_shared(a, ph, a.dpart, b, nb, row, l & 15);
-        }
+    sum_shared<MT>(a, ph, a.dpart, b, s);
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
@@ -656,20 +824,22 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
       }
 }
 
-template <int MT, int FMT, int NS, int NSLOT>
+template <int MT, int FMT, int XL, int NS, int NSLOT>
 __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L) {
   const int l = lane_id();
   const int W = blockIdx.x;
   const int rep = W & (NREP - 1);
   const uint32_t* page = a.ctrl + PAGE0 + rep * PAGE_WORDS;
-  // quantize this workgroup's share of x, then wait for everyone's
-  if (W < a.n_items) {
-    xq_item<FMT>(a, W);
-    drain_memory();
-    raise_flag(a.ctrl, PG_XQ, W);
+  if (!XL) {
+    // quantize this workgroup's share of x, then wait for everyone's
+    if (W < a.n_items) {
+      xq_item<FMT>(a, W);
+      drain_memory();
+      raise_flag(a.ctrl, PG_XQ, W);
+    }
+    wait_flags(page + PG_XQ, a.n_items);
+    if (l == 0) lds_store(&L.xq_ok, 1u);
   }
-  wait_flags(page + PG_XQ, a.n_items);
-  if (l == 0) lds_store(&L.xq_ok, 1u);
 
   int k = 0;
   if (a.mlp && W < a.gu.nwg) {
@@ -725,25 +895,52 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L) 
 // ---------------------------------------------------------------------------
 // The persistent kernel: wavefront 0 syncs, the others stream.
 // ---------------------------------------------------------------------------
-template <int MT, int FMT>
+// XL: Q(x) is built in LDS by every workgroup (no cross-workgroup wait
+// before the first product); otherwise it is built once in the workspace.
+template <int MT, int FMT, int XL>
 __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) {
   using C = Cfg<MT>;
   __shared__ Lds<MT, C::NS, C::NSLOT> L;
+  extern __shared__ __align__(16) uint8_t lds_x[];
   const int wv = uni((int)(threadIdx.x >> 6));
   if (threadIdx.x == 0) {
     for (int i = 0; i < C::NSLOT; ++i) L.arrived[i] = 0u;
     L.consumed = 0u;
-    L.xq_ok = 0u;
+    L.xq_ok = XL ? 1u : 0u;
     L.dn_ok = 0u;
   }
   __syncthreads();
   if (wv == 0) {
-    sync_wave<MT, FMT>(a, L);
+    if (XL) {
+      XqLocal<FMT> xq;
+      xq.load(a);
+      xq.finish(a, lds_x, 16 * MT);
+      __syncthreads();
+    }
+    sync_wave<MT, FMT, XL>(a, L);
   } else {
-    Streamer<MT, FMT, C::P> st(a, wv - 1);
+    Streamer<MT, FMT, C::P, XL> st(a, wv - 1, lds_x);
     int k = 0;
-    if (a.mlp) st.template run_phase<true>(L, k);
-    st.template run_phase<false>(L, k);
+    PhaseState s1;
+    XqLocal<FMT> xq;
+    if (XL) xq.load(a);
+    if (a.mlp)
+      st.template begin<true>(s1);
+    else
+      st.template begin<false>(s1);
+    // the first weights are in flight while x is quantized
+    if (XL) {
+      xq.finish(a, lds_x, 16 * MT);
+      __syncthreads();
+    }
+    if (a.mlp) {
+      st.template body<true>(s1, L, k);
+      PhaseState s2;
+      st.template begin<false>(s2);
+      st.template body<false>(s2, L, k);
+    } else {
+      st.template body<false>(s1, L, k);
+    }
   }
 }
 
@@ -810,24 +1007,42 @@ Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp, int G) {
   return p;
 }
 
-template <int MT, int FMT>
-const void* kernel_ptr() { return reinterpret_cast<const void*>(&stream_kernel<MT, FMT>); }
+template <int MT, int FMT, int XL>
+const void* kernel_ptr() { return reinterpret_cast<const void*>(&stream_kernel<MT, FMT, XL>); }
 
-const void* pick_kernel(int MT, int fmt) {
-  if (fmt == FMT_BLOCK) {
-    switch (MT) {
-      case 1: return kernel_ptr<1, FMT_BLOCK>();
-      case 2: return kernel_ptr<2, FMT_BLOCK>();
-      case 4: return kernel_ptr<4, FMT_BLOCK>();
-      default: return kernel_ptr<8, FMT_BLOCK>();
-    }
+// Kernel variants: (MT, XL) in (1,0) (1,1) (2,0) (2,1) (4,0) (8,0).
+constexpr int NVAR = 6;
+int var_index(int MT, int XL) { return MT == 1 ? XL : MT == 2 ? 2 + XL : MT == 4 ? 4 : 5; }
+
+template <int FMT>
+const void* pick_fmt(int vi) {
+  switch (vi) {
+    case 0: return kernel_ptr<1, FMT, 0>();
+    case 1: return kernel_ptr<1, FMT, 1>();
+    case 2: return kernel_ptr<2, FMT, 0>();
+    case 3: return kernel_ptr<2, FMT, 1>();
+    case 4: return kernel_ptr<4, FMT, 0>();
+    default: return kernel_ptr<8, FMT, 0>();
   }
+}
+const void* pick_kernel(int MT, int fmt, int XL) {
+  const int vi = var_index(MT, XL);
+  return fmt == FMT_BLOCK ? pick_fmt<FMT_BLOCK>(vi) : pick_fmt<FMT_MX>(vi);
+}
+
+constexpr int LDS_PER_WG = 163840;  // gfx950: 160 KB of LDS per workgroup
+size_t static_lds(int MT) {
   switch (MT) {
-    case 1: return kernel_ptr<1, FMT_MX>();
-    case 2: return kernel_ptr<2, FMT_MX>();
-    case 4: return kernel_ptr<4, FMT_MX>();
-    default: return kernel_ptr<8, FMT_MX>();
+    case 1: return sizeof(Lds<1, Cfg<1>::NS, Cfg<1>::NSLOT>);
+    case 2: return sizeof(Lds<2, Cfg<2>::NS, Cfg<2>::NSLOT>);
+    case 4: return sizeof(Lds<4, Cfg<4>::NS, Cfg<4>::NSLOT>);
+    default: return sizeof(Lds<8, Cfg<8>::NS, Cfg<8>::NSLOT>);
   }
+}
+// Q(x) goes to LDS when it fits beside the partial-sum slots (with margin).
+bool use_xl(int fmt, int MT, int K1) {
+  if (MT > 2) return false;
+  return static_lds(MT) + (size_t)xl_bytes(fmt, 16 * MT, K1) + 1024 <= (size_t)LDS_PER_WG;
 }
 
 // Workgroups resident at once on the current device for each kernel variant
@@ -836,15 +1051,17 @@ const void* pick_kernel(int MT, int fmt) {
 struct Occupancy {
   std::mutex mu;
   int cus[64] = {0};
-  int per_cu[64][2][4] = {};
+  int per_cu[64][2][NVAR] = {};
 };
 Occupancy g_occ;
 
-int grid_size(int MT, int fmt, int* out) {
+// The XL variants may use up to all LDS the static part leaves; the
+// occupancy is taken at that maximum, so it holds for any smaller use.
+int grid_size(int MT, int fmt, int XL, int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SGD_EHIP;
   const int fi = fmt == FMT_BLOCK ? 0 : 1;
-  const int mi = MT == 1 ? 0 : MT == 2 ? 1 : MT == 4 ? 2 : 3;
+  const int vi = var_index(MT, XL);
   std::lock_guard<std::mutex> lock(g_occ.mu);
   if (g_occ.cus[dev] == 0) {
     int cus = 0;
@@ -852,15 +1069,18 @@ int grid_size(int MT, int fmt, int* out) {
       return SGD_EHIP;
     g_occ.cus[dev] = cus;
   }
-  if (g_occ.per_cu[dev][fi][mi] == 0) {
+  if (g_occ.per_cu[dev][fi][vi] == 0) {
+    const void* kern = pick_kernel(MT, fmt, XL);
+    const int dyn = XL ? LDS_PER_WG - (int)static_lds(MT) : 0;
+    if (XL && hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess)
+      return SGD_EHIP;
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, pick_kernel(MT, fmt), 64 * cfg_nwave(MT), 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 64 * cfg_nwave(MT), (size_t)dyn) != hipSuccess ||
         nb <= 0)
       return SGD_EHIP;
-    g_occ.per_cu[dev][fi][mi] = nb;
+    g_occ.per_cu[dev][fi][vi] = nb;
   }
-  *out = g_occ.cus[dev] * g_occ.per_cu[dev][fi][mi];
+  *out = g_occ.cus[dev] * g_occ.per_cu[dev][fi][vi];
   return SGD_OK;
 }
 
@@ -875,8 +1095,10 @@ size_t stream_workspace_bytes(int fmt, int M, int K1, int F, int N, int K2, bool
 int launch_stream(const Problem& pr, hipStream_t s) {
   const bool mlp = pr.gate != nullptr;
   const int F = mlp ? pr.gate->N : 0;
+  const int MT = mt_for(pr.M);
+  const int XL = use_xl(pr.fmt, MT, pr.K1) ? 1 : 0;
   int G = 0;
-  int rc = grid_size(mt_for(pr.M), pr.fmt, &G);
+  int rc = grid_size(MT, pr.fmt, XL, &G);
   if (rc != SGD_OK) return rc;
   if (G > MAX_WG) G = MAX_WG;
   const Plan p = make_plan(pr.fmt, pr.M, pr.K1, F, pr.w2->N, pr.w2->K, mlp, G);
@@ -912,12 +1134,13 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.dpart = reinterpret_cast<float*>(ws + p.off_dpart);
   a.G = G;
   a.n_pairs = p.n_pairs;
-  a.n_items = p.n_items;
+  a.n_items = XL ? 0 : p.n_items;
   a.ngroups = p.ngroups;
   a.gu = p.gu;
   a.dn = p.dn;
   void* args[] = {&a};
-  return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, 0, s));
+  const size_t dyn = XL ? (size_t)((xl_bytes(pr.fmt, p.Mpad, pr.K1) + 15) & ~15) : 0;
+  return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt, XL), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, dyn, s));
 }
 
 }  // namespace sgd
