@@ -73,6 +73,9 @@ def main():
     ap.add_argument("--ffn", type=int, default=12288)
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    help="instead of the benchmark, run a plain elementwise copy of this many bytes "
+                         "(read once, written once) three times: the reference for HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -83,11 +86,22 @@ def main():
 
     import numpy as np
     import torch
-    import swiglu_decode_amd as sgd
-    import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 3}))
+        return
+
+    import swiglu_decode_amd as sgd
+    import synth
     ms = [int(m) for m in args.ms.split(",")]
     d, F, fmt = args.d, args.ffn, args.fmt
     wl = synth.Workload("bench", d, F, tuple(ms), (fmt,), 1003)
@@ -145,11 +159,15 @@ def main():
     y_out = {m: ys[m].float().cpu().numpy() for m in ms}
 
     rm = 16 if 16 in ms else ms[0]
-    traffic = read_traffic() if rm == 16 and d == 4096 and F == 12288 and fmt == "mx" else None
+    # counter-measured HBM bytes per launch (when taken with the current kernel
+    # sources), expressed like `achieved`: bytes per launch / live duration
+    tb = read_traffic() if rm == 16 and d == 4096 and F == 12288 and fmt == "mx" else None
+    traffic = round(tb / per_m[rm]["us_per_call"] / 1e3, 1) if tb else None
     roof = dict(bound="hbm", achieved=per_m[rm]["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(per_m[rm]["gbs"] / HBM_PEAK_GBS, 4),
                 traffic=traffic, m=rm, us_per_launch=per_m[rm]["us_per_call"],
-                algorithmic_bytes_per_launch=per_m[rm]["bytes"])
+                algorithmic_bytes_per_launch=per_m[rm]["bytes"],
+                traffic_bytes_per_launch=int(tb) if tb else None)
 
     cpu = None
     parity = None
