@@ -923,7 +923,12 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     int k = 0;
     PhaseState s1;
     XqLocal<FMT> xq;
-    if (XL) xq.load(a);
+    if (XL) {
+      // x first, through an empty memory pipeline: its latency is on the
+      // path to the first product, the weights' latency overlaps it
+      xq.load(a);
+      drain_memory();
+    }
     if (a.mlp)
       st.template begin<true>(s1);
     else
