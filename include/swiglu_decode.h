@@ -141,13 +141,16 @@ int sgd_quantize_act(int fmt, const uint16_t* x_bf16, int M, int K,
 /*
  * The GEMM and MLP kernels need a device workspace for the quantized
  * activations, the SwiGLU intermediate, split-K partial sums and
- * synchronisation counters.  Its first 32 KB are a control block that must
+ * synchronisation counters.  Its first 256 KB are a control block that must
  * be zero-filled ONCE after allocation (sgd_workspace_clear or any fill
  * kernel); every call leaves it zero again on exit, so one workspace can
  * serve calls of any shape that fit in it.  Calls that share a workspace
  * must not overlap (serialise them on one stream).  Size in bytes; 0 on
  * invalid arguments or when the shape needs more counters than the control
- * block holds (16 + ffn/16 + ffn/64 + N/32 words must be <= 8192).
+ * block holds (the output width N, or d of the MLP, must be <= 860160).
+ * The size does not depend on the device.  The kernels assume that all of
+ * their workgroups can be resident at once (they size the grid so), so a
+ * second persistent launch must not run concurrently on the same device.
  */
 size_t sgd_gemm_workspace_bytes(int fmt, int M, int N, int K);
 size_t sgd_mlp_workspace_bytes(int fmt, int M, int d, int ffn);

@@ -174,14 +174,6 @@ __device__ __forceinline__ void lds_wait_geq(const uint32_t* p, uint32_t target)
 // ---------------------------------------------------------------------------
 // Streaming wavefront
 // ---------------------------------------------------------------------------
-// Where a phase's chunk walk stands.
-struct PhaseState {
-  int active;     // this workgroup has chunks in the phase
-  int c, c1;      // this wavefront's next chunk; end of the workgroup's range
-  int bf, bl;     // first and last band of the range
-  ChunkPos cp;    // position of chunk c
-};
-
 // LDS copy of Q(x) (used when it fits): codes [Mpad][K1 + 16] (rows padded
 // by 16 bytes so the 16 rows of an operand load fall in distinct banks), then
 // the scales: block fp32 [K1/128][Mpad]; mx E8M0 [Mpad][K1/32].
@@ -191,22 +183,28 @@ __host__ __device__ constexpr int xl_bytes(int fmt, int Mpad, int K1) {
   return xl_scale_offset(Mpad, K1) + (fmt == FMT_BLOCK ? (K1 / 128) * Mpad * 4 : Mpad * (K1 / 32));
 }
 
-template <int MT, int FMT, int P, int XL>
-struct Streamer {
-  const Args& a;
-  const int q;  // index among the workgroup's streaming wavefronts
-  const uint8_t* lx;  // LDS copy of Q(x) (XL)
-  // ring: weights of stream 0/1 and their scale words (block: fp32 bits in
-  // S0; mx: S0/S1 = dwords holding this lane's two 32-column-block scales for
-  // gate/up, its own scale slot for the second GEMM), fp8 activations (one
-  // 32-byte operand per m-tile) and their scales (block: rows 4*(l/16)..+3
-  // as v4f; mx: gate/up: this lane's two 32-column-block bytes, second GEMM:
-  // its own scale slot in X0)
+// One wavefront's ring of P slots: weights of stream 0/1 and their scale
+// words (block: fp32 bits in S0; mx: S0/S1 = dwords holding this lane's two
+// 32-column-block scales for gate/up, its own scale slot for the second
+// GEMM), fp8 activations (one 32-byte operand per m-tile) and their scales
+// (block: rows 4*(l/16)..+3 as v4f; mx: gate/up: this lane's two
+// 32-column-block bytes, second GEMM: its own scale slot in X0).  Each phase
+// has a ring of its own.
+template <int MT, int P>
+struct Ring {
   v8i RB[P][2];
   uint32_t S0[P][2], S1[P][2];
   v8i RA[P][MT];
   v4f XB[P][MT];
   uint32_t X0[P][MT], X1[P][MT];
+};
+
+template <int MT, int FMT, int P, int XL>
+struct Streamer {
+  using R_t = Ring<MT, P>;
+  const Args& a;
+  const int q;  // index among the workgroup's streaming wavefronts
+  const uint8_t* lx;  // LDS copy of Q(x) (XL)
   // buffer resources of the current phase
   __amdgpu_buffer_rsrc_t rw0, rw1, rs0, rs1, rx, rxs;
   // lane constants
@@ -267,7 +265,7 @@ struct Streamer {
 
   // ---- loads of one ring slot (unconditional: fillers read past the end) ----
   template <bool GU>
-  __device__ __forceinline__ void load_b(int s, const ChunkPos& cp, int KT, int k) {
+  __device__ __forceinline__ void load_b(R_t& R, int s, const ChunkPos& cp, int KT, int k) {
     const int kt_ = cp.kt0 + k;
     const bool ok = cp.ok && kt_ < KT;
     const uint32_t kt = ok ? (uint32_t)kt_ : 0u;
@@ -276,31 +274,31 @@ struct Streamer {
     const uint32_t uKT = (uint32_t)KT;
     const uint32_t t0 = ok ? (n0 * uKT + kt) * 2048u + lo16 : OOB;
     const uint32_t t1 = ok ? (n1 * uKT + kt) * 2048u + lo16 : OOB;
-    RB[s][0] = make_v8i(ld4(rw0, t0), ld4(rw0, t0 + 1024u));
-    RB[s][1] = make_v8i(ld4(rw1, t1), ld4(rw1, t1 + 1024u));
+    R.RB[s][0] = make_v8i(ld4(rw0, t0), ld4(rw0, t0 + 1024u));
+    R.RB[s][1] = make_v8i(ld4(rw1, t1), ld4(rw1, t1 + 1024u));
     if (FMT == FMT_BLOCK) {
       const uint32_t o0 = ok ? ((n0 >> 3) * uKT + kt) * 4u : OOB;
       const uint32_t o1 = ok ? ((n1 >> 3) * uKT + kt) * 4u : OOB;
-      S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, o0, 0, 0);
-      S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, o1, 0, 0);
+      R.S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, o0, 0, 0);
+      R.S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, o1, 0, 0);
     } else {
       const uint32_t KG = (uKT + 3u) >> 2;
       const uint32_t g0 = (n0 * KG + (kt >> 2)) * 256u;
       const uint32_t g1 = (n1 * KG + (kt >> 2)) * 256u;
       if (GU) {
-        S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_gu0 : OOB, 0, 0);
-        S1[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_gu1 : OOB, 0, 0);
-        S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_gu0 : OOB, 0, 0);
-        S1[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_gu1 : OOB, 0, 0);
+        R.S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_gu0 : OOB, 0, 0);
+        R.S1[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_gu1 : OOB, 0, 0);
+        R.S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_gu0 : OOB, 0, 0);
+        R.S1[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_gu1 : OOB, 0, 0);
       } else {
-        S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_dn : OOB, 0, 0);
-        S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_dn : OOB, 0, 0);
+        R.S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_dn : OOB, 0, 0);
+        R.S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_dn : OOB, 0, 0);
       }
     }
   }
 
   template <bool GU>
-  __device__ __forceinline__ void load_a(int s, const ChunkPos& cp, int KT, int k) {
+  __device__ __forceinline__ void load_a(R_t& R, int s, const ChunkPos& cp, int KT, int k) {
     const int kt_ = cp.kt0 + k;
     const bool ok = cp.ok && kt_ < KT;
     const uint32_t kt = ok ? (uint32_t)kt_ : 0u;
@@ -313,16 +311,16 @@ struct Streamer {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const uint8_t* p = lx + (mt * 16 + (l & 15)) * rs + kt * 128 + 16 * (l >> 4);
-        RA[s][mt] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+        R.RA[s][mt] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
         if (FMT == FMT_BLOCK) {
-          XB[s][mt] = *reinterpret_cast<const v4f*>(sc + (kt * (16 * MT) + 16 * mt + 4 * (l >> 4)) * 4);
+          R.XB[s][mt] = *reinterpret_cast<const v4f*>(sc + (kt * (16 * MT) + 16 * mt + 4 * (l >> 4)) * 4);
         } else {
           const uint8_t* e = sc + (mt * 16 + (l & 15)) * (a.K1 >> 5) + 4 * kt;
           if (GU) {
-            X0[s][mt] = e[(l >> 4) >> 1];
-            X1[s][mt] = e[2 + ((l >> 4) >> 1)];
+            R.X0[s][mt] = e[(l >> 4) >> 1];
+            R.X1[s][mt] = e[2 + ((l >> 4) >> 1)];
           } else {
-            X0[s][mt] = e[l >> 4];
+            R.X0[s][mt] = e[l >> 4];
           }
         }
       }
@@ -331,14 +329,14 @@ struct Streamer {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint32_t o = ok ? (GU ? xa_lane : aq_lane) + (uint32_t)mt * 16u * Kd + kt * 128u : OOB;
-      RA[s][mt] = make_v8i(ld4(rx, o), ld4(rx, ok ? o + 64u : OOB));
+      R.RA[s][mt] = make_v8i(ld4(rx, o), ld4(rx, ok ? o + 64u : OOB));
       if (FMT == FMT_BLOCK) {
         const uint32_t so = (GU ? xs_lane : as_lane) + (kt * (uint32_t)a.Mpad + 16u * (uint32_t)mt) * 4u;
-        XB[s][mt] = ld_coherent_v4f(rxs, ok ? so : OOB);
+        R.XB[s][mt] = ld_coherent_v4f(rxs, ok ? so : OOB);
       } else {
         const uint32_t so = (GU ? xs_lane : as_lane) + (uint32_t)mt * 16u * (Kd >> 5) + kt * 4u;
-        X0[s][mt] = ld_coherent_u8(rxs, ok ? so : OOB);
-        if (GU) X1[s][mt] = ld_coherent_u8(rxs, ok ? so + 2u : OOB);
+        R.X0[s][mt] = ld_coherent_u8(rxs, ok ? so : OOB);
+        if (GU) R.X1[s][mt] = ld_coherent_u8(rxs, ok ? so + 2u : OOB);
       }
     }
   }
@@ -360,17 +358,17 @@ struct Streamer {
   // ~13 bits below the largest product of a group (measured on gfx950); that
   // ~1e-5 relative error would flip fp8 codes of the re-quantized product,
   // while the bf16 instruction's sums are fp32-accurate.
-  __device__ __forceinline__ void step_gu(int s, int kt, v4f (&acc)[2][MT]) {
+  __device__ __forceinline__ void step_gu(R_t& R, int s, int kt, v4f (&acc)[2][MT]) {
     const int sh = 8 * (kt & 3);
     v8bf av[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       float s0 = 1.0f, s1 = 1.0f;
       if (FMT == FMT_MX) {
-        s0 = pow2_pos((int)X0[s][mt] - 127);
-        s1 = pow2_pos((int)X1[s][mt] - 127);
+        s0 = pow2_pos((int)R.X0[s][mt] - 127);
+        s1 = pow2_pos((int)R.X1[s][mt] - 127);
       }
-      const v8i x = RA[s][mt];
+      const v8i x = R.RA[s][mt];
       av[mt][0] = widen8((uint32_t)x[0], (uint32_t)x[1], s0);
       av[mt][1] = widen8((uint32_t)x[2], (uint32_t)x[3], s0);
       av[mt][2] = widen8((uint32_t)x[4], (uint32_t)x[5], s1);
@@ -380,10 +378,10 @@ struct Streamer {
     for (int nb = 0; nb < 2; ++nb) {
       float s0 = 1.0f, s1 = 1.0f;
       if (FMT == FMT_MX) {
-        s0 = pow2_pos((int)((S0[s][nb] >> sh) & 0xFFu) - 127);
-        s1 = pow2_pos((int)((S1[s][nb] >> sh) & 0xFFu) - 127);
+        s0 = pow2_pos((int)((R.S0[s][nb] >> sh) & 0xFFu) - 127);
+        s1 = pow2_pos((int)((R.S1[s][nb] >> sh) & 0xFFu) - 127);
       }
-      const v8i w = RB[s][nb];
+      const v8i w = R.RB[s][nb];
       v8bf b[4];
       b[0] = widen8((uint32_t)w[0], (uint32_t)w[1], s0);
       b[1] = widen8((uint32_t)w[2], (uint32_t)w[3], s0);
@@ -395,7 +393,7 @@ struct Streamer {
           v4f t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[i], t, 0, 0, 0);
-          acc[nb][mt] += t * (XB[s][mt] * __uint_as_float(S0[s][nb]));
+          acc[nb][mt] += t * (R.XB[s][mt] * __uint_as_float(R.S0[s][nb]));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -406,19 +404,19 @@ struct Streamer {
   }
 
   // Second GEMM: scaled fp8 MFMA (MX scales in the instruction).
-  __device__ __forceinline__ void step_dn(int s, int kt, v4f (&acc)[2][MT]) {
+  __device__ __forceinline__ void step_dn(R_t& R, int s, int kt, v4f (&acc)[2][MT]) {
     const int sh = 8 * (kt & 3);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const v8i av = RA[s][mt];
+        const v8i av = R.RA[s][mt];
         if (FMT == FMT_BLOCK) {
           const v4f z = {0.f, 0.f, 0.f, 0.f};
-          const v4f t = mfma_f8(av, RB[s][nb], z, 127, 127);
-          acc[nb][mt] += t * (XB[s][mt] * __uint_as_float(S0[s][nb]));
+          const v4f t = mfma_f8(av, R.RB[s][nb], z, 127, 127);
+          acc[nb][mt] += t * (R.XB[s][mt] * __uint_as_float(R.S0[s][nb]));
         } else {
-          acc[nb][mt] = mfma_f8(av, RB[s][nb], acc[nb][mt], (int)X0[s][mt], (int)(S0[s][nb] >> sh));
+          acc[nb][mt] = mfma_f8(av, R.RB[s][nb], acc[nb][mt], (int)R.X0[s][mt], (int)(R.S0[s][nb] >> sh));
         }
       }
     }
@@ -437,40 +435,33 @@ struct Streamer {
       __hip_atomic_fetch_add(&L.arrived[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 
-  // Start a phase: find this workgroup's chunks and fill the ring with the
-  // weights of this wavefront's first chunk.
-  template <bool GU>
-  __device__ __forceinline__ void begin(PhaseState& st) {
+  // Stream this workgroup's chunks of one phase.  The ring is filled with the
+  // weights of this wavefront's first chunk before `between()` runs (the
+  // workgroup-wide x quantization, when there is one; every wavefront calls
+  // it exactly once), and with activations after it.
+  template <bool GU, int NS, int NSLOT, class Between>
+  __device__ __forceinline__ void run_phase(Lds<MT, NS, NSLOT>& L, int& k, Between between) {
     const Phase& ph = GU ? a.gu : a.dn;
     const int W = blockIdx.x;
-    st.active = 0;
-    if (W >= ph.nwg) return;
-    const int c0 = range_start(ph, W);
-    st.c1 = range_start(ph, W + 1);
-    if (c0 >= st.c1) return;
-    st.active = 1;
-    st.c = c0 + q;
-    st.bf = c0 / ph.CPB;
-    st.bl = (st.c1 - 1) / ph.CPB;
+    if (!(W < ph.nwg && range_start(ph, W) < range_start(ph, W + 1))) {
+      between();
+      return;
+    }
+    const int c0 = range_start(ph, W), c1 = range_start(ph, W + 1);
+    const int KT = ph.KT;
+    int c = c0 + q;
     make_resources(GU);
-    st.cp = chunk_pos<P>(ph, st.c, st.c1);
+    R_t R;
+    ChunkPos cp = chunk_pos<P>(ph, c, c1);
 #pragma unroll
-    for (int s = 0; s < P; ++s) load_b<GU>(s, st.cp, ph.KT, s);
-  }
-
-  // Stream the rest of the phase.
-  template <bool GU, int NS, int NSLOT>
-  __device__ __forceinline__ void body(PhaseState& st, Lds<MT, NS, NSLOT>& L, int& k) {
-    if (!st.active) return;
-    const Phase& ph = GU ? a.gu : a.dn;
-    const int KT = ph.KT, c1 = st.c1;
-    int c = st.c;
-    ChunkPos cp = st.cp;
+    for (int s = 0; s < P; ++s) load_b<GU>(R, s, cp, KT, s);
+    between();
     // activations only once they exist (the LDS copy of Q(x) already does)
     if (!(XL && (GU || !a.mlp))) lds_wait_geq(GU || !a.mlp ? &L.xq_ok : &L.dn_ok, 1u);
 #pragma unroll
-    for (int s = 0; s < P; ++s) load_a<GU>(s, cp, KT, s);
-    for (int b = st.bf; b <= st.bl; ++b) {
+    for (int s = 0; s < P; ++s) load_a<GU>(R, s, cp, KT, s);
+    const int bf = c0 / ph.CPB, bl = (c1 - 1) / ph.CPB;
+    for (int b = bf; b <= bl; ++b) {
       const int hi = min(c1, (b + 1) * ph.CPB);
       v4f acc[2][MT];
 #pragma unroll
@@ -485,12 +476,12 @@ struct Streamer {
           const int kt = cp.kt0 + s;
           if (kt < KT) {
             if (GU)
-              step_gu(s, kt, acc);
+              step_gu(R, s, kt, acc);
             else
-              step_dn(s, kt, acc);
+              step_dn(R, s, kt, acc);
           }
-          load_b<GU>(s, np, KT, s);
-          load_a<GU>(s, np, KT, s);
+          load_b<GU>(R, s, np, KT, s);
+          load_a<GU>(R, s, np, KT, s);
         }
         c = cn;
         cp = np;
@@ -921,7 +912,6 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
   } else {
     Streamer<MT, FMT, C::P, XL> st(a, wv - 1, lds_x);
     int k = 0;
-    PhaseState s1;
     XqLocal<FMT> xq;
     if (XL) {
       // x first, through an empty memory pipeline: its latency is on the
@@ -929,22 +919,19 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
       xq.load(a);
       drain_memory();
     }
-    if (a.mlp)
-      st.template begin<true>(s1);
-    else
-      st.template begin<false>(s1);
     // the first weights are in flight while x is quantized
-    if (XL) {
-      xq.finish(a, lds_x, 16 * MT);
-      __syncthreads();
-    }
+    auto quantize_x = [&]() {
+      if (XL) {
+        xq.finish(a, lds_x, 16 * MT);
+        __syncthreads();
+      }
+    };
+    auto nothing = []() {};
     if (a.mlp) {
-      st.template body<true>(s1, L, k);
-      PhaseState s2;
-      st.template begin<false>(s2);
-      st.template body<false>(s2, L, k);
+      st.template run_phase<true>(L, k, quantize_x);
+      st.template run_phase<false>(L, k, nothing);
     } else {
-      st.template body<false>(s1, L, k);
+      st.template run_phase<false>(L, k, quantize_x);
     }
   }
 }
