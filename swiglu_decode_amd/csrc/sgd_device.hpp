@@ -208,6 +208,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ v4f ld_coherent_v4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX_SC1));
 }
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+// 16-byte agent-coherent (write-through) store through a buffer resource.
+__device__ __forceinline__ void st_coherent_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  const v4u d = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, AUX_SC1);
+}
 __device__ __forceinline__ uint32_t ld_coherent_u8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, AUX_SC1);
 }

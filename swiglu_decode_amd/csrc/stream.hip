@@ -494,23 +494,6 @@ struct Streamer {
 // ---------------------------------------------------------------------------
 // Sync wavefront
 // ---------------------------------------------------------------------------
-// Store one quantized 128-column group of one row with agent-coherent 32-bit
-// stores: codes (lane l holds elements 2l, 2l+1; even lanes write four) and
-// the group's scale(s).
-template <int FMT>
-__device__ __forceinline__ void store_group(uint8_t* codes_at_group, uint32_t c, float sf, uint32_t se,
-                                            float* sbl_at, uint8_t* smx_at) {
-  const int l = lane_id();
-  const uint32_t up = __shfl_down(c, 1, WAVE);
-  if ((l & 1) == 0) st_coherent(reinterpret_cast<uint32_t*>(codes_at_group + 2 * l), (c & 0xFFFFu) | (up << 16));
-  if (FMT == FMT_BLOCK) {
-    if (l == 0) st_coherent(sbl_at, sf);
-  } else {
-    const uint32_t e1 = __shfl(se, 16, WAVE), e2 = __shfl(se, 32, WAVE), e3 = __shfl(se, 48, WAVE);
-    if (l == 0) st_coherent(reinterpret_cast<uint32_t*>(smx_at), se | (e1 << 8) | (e2 << 16) | (e3 << 24));
-  }
-}
-
 // Block-format scales live in [groups][Mpad]; rows M..Mpad-1 hold zero.
 __device__ __forceinline__ void zero_pad_scales(float* col_of_group, int M, int Mpad) {
   const int l = lane_id();
@@ -518,13 +501,68 @@ __device__ __forceinline__ void zero_pad_scales(float* col_of_group, int M, int 
   if (l + 64 >= M && l + 64 < Mpad) st_coherent(col_of_group + l + 64, 0.0f);
 }
 
+// Quantize one 32-element block held by one lane (one row, 32 consecutive
+// columns): the 32 E4M3 codes in element order (8 dwords) and the block's
+// scale.  Block format: the scale covers a 128-column group, whose 4 blocks
+// sit in 4 consecutive lanes that are all active (amax over the group);
+// returned in *sf.  MX: the E8M0 byte of this block, in *se.  E4M3
+// conversion in hardware after clamping to +-448 (round to nearest even,
+// checked against the integer encoder over 6.8e8 fp32 patterns on gfx950).
+template <int FMT>
+__device__ __forceinline__ void quant_block32(const float (&v)[32], uint32_t (&cw)[8], float* sf, uint32_t* se) {
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(v[e]));
+  float mul = 1.0f, s = 1.0f;
+  if (FMT == FMT_BLOCK) {
+    am = fmaxf(am, __shfl_xor(am, 1, WAVE));
+    am = fmaxf(am, __shfl_xor(am, 2, WAVE));
+    s = block_scale(am);
+  } else {
+    const int X = mx_exponent(am);
+    mul = pow2_neg(X);
+    *se = (uint32_t)(X + 127);
+  }
+  *sf = s;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float t = FMT == FMT_BLOCK ? v[4 * c + e] / s : v[4 * c + e] * mul;
+      q[e] = __builtin_amdgcn_fmed3f(t, -E4M3_MAX, E4M3_MAX);
+    }
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+    cw[c] = (uint32_t)w;
+  }
+}
+
+// The four E8M0 bytes of the lanes 4q..4q+3 packed into one word (lane 4q's
+// byte lowest), valid in every lane of the four.
+__device__ __forceinline__ uint32_t pack4_lanes(uint32_t e) {
+  const int base = lane_id() & ~3;
+  return __shfl(e, base, WAVE) | (__shfl(e, base + 1, WAVE) << 8) | (__shfl(e, base + 2, WAVE) << 16) |
+         (__shfl(e, base + 3, WAVE) << 24);
+}
+
+__device__ __forceinline__ void bf16x32_to_f32(const uint4 (&w)[4], float (&v)[32]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * c + 2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
+      v[8 * c + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+    }
+  }
+}
+
 // All wavefronts of a workgroup quantize x into LDS (layout above): one lane
 // per (row, 32-column block).  The loads of a lane's first four blocks are
 // issued before the wavefront's first weight loads, so waiting for them does
 // not wait for the weights (the load counter completes in issue order).
-// E4M3 conversion in hardware after clamping to +-448 (round to nearest
-// even, checked against the integer encoder over 6.8e8 fp32 patterns on
-// gfx950).  Rows M..Mpad-1 become zero codes with zero scales.
+// Rows M..Mpad-1 become zero codes with zero scales.
 template <int FMT>
 struct XqLocal {
   static constexpr int U = 4;  // blocks per lane whose loads go first
@@ -550,42 +588,14 @@ struct XqLocal {
     const int r = i / nb, j = i - r * nb;
     uint8_t* sc = lx + xl_scale_offset(Mpad, a.K1);
     float v[32];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * c + 2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
-        v[8 * c + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
-      }
-    }
-    float am = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(v[e]));
-    float mul = 1.0f, sf = 1.0f;
+    bf16x32_to_f32(w, v);
+    uint32_t cw[8], se = 0;
+    float sf = 1.0f;
+    quant_block32<FMT>(v, cw, &sf, &se);
     if (FMT == FMT_BLOCK) {
-      // the 4 blocks of a 128-column group sit in 4 consecutive lanes
-      am = fmaxf(am, __shfl_xor(am, 1, WAVE));
-      am = fmaxf(am, __shfl_xor(am, 2, WAVE));
-      sf = block_scale(am);
       if ((j & 3) == 0) reinterpret_cast<float*>(sc)[(j >> 2) * Mpad + r] = sf;
     } else {
-      const int X = mx_exponent(am);
-      mul = pow2_neg(X);
-      sc[r * nb + j] = (uint8_t)(X + 127);
-    }
-    uint32_t cw[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float q[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float t = FMT == FMT_BLOCK ? v[4 * c + e] / sf : v[4 * c + e] * mul;
-        q[e] = __builtin_amdgcn_fmed3f(t, -E4M3_MAX, E4M3_MAX);
-      }
-      int wv = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-      wv = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], wv, true);
-      cw[c] = (uint32_t)wv;
+      sc[r * nb + j] = (uint8_t)se;
     }
     uint4* dst = reinterpret_cast<uint4*>(lx + r * xl_row_stride(a.K1) + 32 * j);
     dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
@@ -622,57 +632,76 @@ struct XqLocal {
   }
 };
 
-// Quantize x for one item: its (128-column group, 16-row tile) pairs.
+// Quantize x into the workspace for one item: its (128-column group,
+// 16-row tile) pairs, one lane per (row, 32-column block).
 template <int FMT>
 __device__ __forceinline__ void xq_item(const Args& a, int item) {
   const int l = lane_id();
   const int MTa = a.Mpad >> 4;
   const int p0 = (int)(((long long)item * a.n_pairs) / a.n_items);
   const int p1 = (int)(((long long)(item + 1) * a.n_pairs) / a.n_items);
+  const __amdgpu_buffer_rsrc_t rxa = make_rsrc(a.xa, (uint32_t)a.M * (uint32_t)a.K1);
   for (int p = p0; p < p1; ++p) {
     const int kg = p / MTa, mt = p - kg * MTa;
-    const int r0 = mt * 16, nr = min(16, a.M - r0);
-    uint32_t pr[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      pr[i] = *reinterpret_cast<const uint32_t*>(a.x + (size_t)min(r0 + i, a.M - 1) * a.K1 + kg * 128 + 2 * l);
+    const int row = mt * 16 + (l >> 2), j = l & 3;
     float* sbl = static_cast<float*>(a.xs) + (size_t)kg * a.Mpad;
+    if (row < a.M) {  // the 4 lanes of a row agree
+      const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K1 + kg * 128 + 32 * j);
+      uint4 w[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < nr) {
-        const int row = r0 + i;
-        float sf = 1.0f;
-        uint32_t se = 0;
-        const uint32_t c = quant_pair<FMT>(bf16_to_f32(pr[i] & 0xFFFFu), bf16_to_f32(pr[i] >> 16), &sf, &se);
-        store_group<FMT>(a.xa + (size_t)row * a.K1 + kg * 128, c, sf, se, sbl + row,
-                         static_cast<uint8_t*>(a.xs) + (size_t)row * (a.K1 >> 5) + 4 * kg);
+      for (int c = 0; c < 4; ++c) w[c] = src[c];
+      float v[32];
+      bf16x32_to_f32(w, v);
+      uint32_t cw[8], se = 0;
+      float sf = 1.0f;
+      quant_block32<FMT>(v, cw, &sf, &se);
+      const uint32_t off = (uint32_t)row * (uint32_t)a.K1 + (uint32_t)(kg * 128 + 32 * j);
+      st_coherent_b128(rxa, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
+      st_coherent_b128(rxa, off + 16u, make_uint4(cw[4], cw[5], cw[6], cw[7]));
+      if (FMT == FMT_BLOCK) {
+        if (j == 0) st_coherent(sbl + row, sf);
+      } else {
+        const uint32_t e4 = pack4_lanes(se);
+        if (j == 0)
+          st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.xs) + (size_t)row * (a.K1 >> 5) + 4 * kg), e4);
       }
     }
     if (FMT == FMT_BLOCK && mt == MTa - 1) zero_pad_scales(sbl, a.M, a.Mpad);
   }
 }
 
-// Re-quantize 128-column group g of a = silu(g)*u, 16 rows per batch (all
-// loads of a batch are in flight together).
+// Re-quantize 128-column group g of a = silu(g)*u (fp32, written by other
+// workgroups: read agent-coherently), one lane per (row, 32-column block).
 template <int FMT>
 __device__ __forceinline__ void requant_group(const Args& a, int g) {
   const int l = lane_id();
-  for (int r0 = 0; r0 < a.M; r0 += 16) {
-    uint64_t v[16];
+  const __amdgpu_buffer_rsrc_t r32 = make_rsrc(a.a32, (uint32_t)a.M * (uint32_t)a.F * 4u);
+  const __amdgpu_buffer_rsrc_t raq = make_rsrc(a.aq, (uint32_t)a.M * (uint32_t)a.F);
+  for (int i = l; i < a.M * 4; i += 64) {  // (M*4 is a multiple of 4: the 4 lanes of a row agree)
+    const int r = i >> 2, j = i & 3;
+    const uint32_t col = (uint32_t)(g * 128 + 32 * j);
+    const uint32_t base = ((uint32_t)r * (uint32_t)a.F + col) * 4u;
+    float v[32];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v[i] = ld_coherent(reinterpret_cast<const uint64_t*>(a.a32 + (size_t)min(r0 + i, a.M - 1) * a.F + g * 128 + 2 * l));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = r0 + i;
-      if (row < a.M) {
-        float sf = 1.0f;
-        uint32_t se = 0;
-        const uint32_t c = quant_pair<FMT>(__uint_as_float((uint32_t)v[i]), __uint_as_float((uint32_t)(v[i] >> 32)), &sf, &se);
-        store_group<FMT>(a.aq + (size_t)row * a.F + g * 128, c, sf, se,
-                         static_cast<float*>(a.as) + (size_t)g * a.Mpad + row,
-                         static_cast<uint8_t*>(a.as) + (size_t)row * (a.F >> 5) + 4 * g);
-      }
+    for (int c = 0; c < 8; ++c) {
+      const v4f t = ld_coherent_v4f(r32, base + 16u * c);
+      v[4 * c] = t[0];
+      v[4 * c + 1] = t[1];
+      v[4 * c + 2] = t[2];
+      v[4 * c + 3] = t[3];
+    }
+    uint32_t cw[8], se = 0;
+    float sf = 1.0f;
+    quant_block32<FMT>(v, cw, &sf, &se);
+    const uint32_t off = (uint32_t)r * (uint32_t)a.F + col;
+    st_coherent_b128(raq, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
+    st_coherent_b128(raq, off + 16u, make_uint4(cw[4], cw[5], cw[6], cw[7]));
+    if (FMT == FMT_BLOCK) {
+      if (j == 0) st_coherent(static_cast<float*>(a.as) + (size_t)g * a.Mpad + r, sf);
+    } else {
+      const uint32_t e4 = pack4_lanes(se);
+      if (j == 0)
+        st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.as) + (size_t)r * (a.F >> 5) + 4 * g), e4);
     }
   }
   if (FMT == FMT_BLOCK) zero_pad_scales(static_cast<float*>(a.as) + (size_t)g * a.Mpad, a.M, a.Mpad);
