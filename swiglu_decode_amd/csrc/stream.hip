@@ -66,6 +66,8 @@ struct Phase {
   int nbands;   // GU: ffn / 16; DN: N / 32
   int nchunks;  // nbands * CPB
   int nwg;      // workgroups the chunks are dealt to
+  int nunits;   // ranges are dealt in units of upc chunks: nunits * upc = nchunks
+  int upc;      // (upc = CPB: whole bands, no band shared by two workgroups; 1: chunks)
 };
 
 struct Args {
@@ -87,8 +89,8 @@ struct Args {
   float* a32;                // [M, F] silu(g) * u
   uint8_t* aq;               // [M, F] codes of Q(a)
   void* as;                  // block fp32 [F/128][Mpad]; mx u8 [M][F/32]
-  float* gpart;              // [G][2][2][M][16] split-K partials of shared GU bands
-  float* dpart;              // [G][2][2][M][16] split-K partials of shared DN bands
+  float* gpart;              // split-K partials of shared GU bands: [G][2 sides] slots
+  float* dpart;              // split-K partials of shared DN bands: [G][2 sides] slots
   uint32_t scale_bytes_g, scale_bytes_2;  // packed weight-scale sizes
   int G;                     // workgroups in the grid
   int n_pairs, n_items;      // x quantization: (k-group, row tile) pairs, dealt into items
@@ -118,7 +120,7 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // static schedule
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int range_start(const Phase& ph, int W) {
-  return (int)(((long long)W * ph.nchunks) / ph.nwg);
+  return (int)(((long long)W * ph.nunits) / ph.nwg) * ph.upc;
 }
 // The workgroup whose range holds chunk c.
 __device__ __forceinline__ int owner_wg(const Phase& ph, int c) {
@@ -727,29 +729,55 @@ __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Split-K partials of shared bands, slot (workgroup W, side).  Up to two row
+// tiles: [2][M][16] fp32, rows < M only (one row costs two stores).  More:
+// the sync wavefront's sums in their register layout, [2][MT][64 lanes] x
+// v4f, so that each lane moves 16 bytes per (n-block, m-tile).
+template <int MT>
+__device__ __forceinline__ uint32_t part_slot_bytes() { return 2u * MT * 64u * 16u; }
+template <int MT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const Args& a, const float* part) {
+  return make_rsrc(part, (uint32_t)a.G * 2u * part_slot_bytes<MT>());
+}
+
 // Sum of the split-K partials of a shared band over its workgroups, in
 // workgroup order (all of one workgroup's loads in flight together).
-// part: [G][2][2][M][16].
 template <int MT>
 __device__ __forceinline__ void sum_shared(const Args& a, const Phase& ph, const float* part, int b,
                                            v4f (&s)[2][MT]) {
   const int l = lane_id();
+  const __amdgpu_buffer_rsrc_t r = part_rsrc<MT>(a, part);
   const int w0 = owner_wg(ph, b * ph.CPB), w1 = owner_wg(ph, b * ph.CPB + ph.CPB - 1);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) s[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (MT <= 2) {
+    for (int w = w0; w <= w1; ++w) {
+      const float* base = part + ((size_t)w * 2 + band_side(ph, w, b)) * 2 * a.M * 16;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int row = min(mt * 16 + 4 * (l >> 4) + rr, a.M - 1);
+            s[nb][mt][rr] += ld_coherent(base + ((size_t)nb * a.M + row) * 16 + (l & 15));
+          }
+    }
+    return;
+  }
   for (int w = w0; w <= w1; ++w) {
-    const float* base = part + ((size_t)w * 2 + band_side(ph, w, b)) * 2 * a.M * 16;
+    const uint32_t base = ((uint32_t)w * 2u + (uint32_t)band_side(ph, w, b)) * part_slot_bytes<MT>();
+    v4f t[2][MT];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) t[nb][mt] = ld_coherent_v4f(r, base + (uint32_t)(((nb * MT + mt) * 64 + l) * 16));
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = min(mt * 16 + 4 * (l >> 4) + rr, a.M - 1);
-          s[nb][mt][rr] += ld_coherent(base + ((size_t)nb * a.M + row) * 16 + (l & 15));
-        }
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) s[nb][mt] += t[nb][mt];
   }
 }
 
@@ -760,16 +788,27 @@ __device__ __forceinline__ bool arrive_shared(const Args& a, const Phase& ph, fl
                                               const v4f (&s)[2][MT], int nsh) {
   const int l = lane_id();
   const int side = band_side(ph, blockIdx.x, b);
+  if (MT <= 2) {
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = mt * 16 + 4 * (l >> 4) + rr;
-        if (row < a.M)
-          st_coherent(part + ((((size_t)blockIdx.x * 2 + side) * 2 + nb) * a.M + row) * 16 + (l & 15), s[nb][mt][rr]);
-      }
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = mt * 16 + 4 * (l >> 4) + rr;
+          if (row < a.M)
+            st_coherent(part + ((((size_t)blockIdx.x * 2 + side) * 2 + nb) * a.M + row) * 16 + (l & 15),
+                        s[nb][mt][rr]);
+        }
+  } else {
+    const __amdgpu_buffer_rsrc_t r = part_rsrc<MT>(a, part);
+    const uint32_t base = ((uint32_t)blockIdx.x * 2u + (uint32_t)side) * part_slot_bytes<MT>();
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        st_coherent_b128(r, base + (uint32_t)(((nb * MT + mt) * 64 + l) * 16), __builtin_bit_cast(uint4, s[nb][mt]));
+  }
   drain_memory();
   uint32_t old = 0;
   if (l == 0) old = atomic_add_agent(cnt + b, 1u);
@@ -983,14 +1022,24 @@ int cfg_ns(int MT) { return MT == 1 ? Cfg<1>::NS : MT == 2 ? Cfg<2>::NS : MT == 
 int cfg_p(int MT) { return MT == 1 ? Cfg<1>::P : MT == 2 ? Cfg<2>::P : MT == 4 ? Cfg<4>::P : Cfg<8>::P; }
 int cfg_nwave(int MT) { return cfg_ns(MT) + 1; }
 
-Phase make_phase(int KT, int nbands, int P, int NS, int G) {
+// Chunks are dealt in equal contiguous ranges: of whole bands when `whole`
+// (over as few workgroups as give the same number of bands to each), else
+// of chunks (over enough workgroups to keep every streaming wavefront busy).
+Phase make_phase(int KT, int nbands, int P, int NS, int G, bool whole) {
   Phase ph{};
   ph.KT = KT;
   ph.CPB = (KT + P - 1) / P;
   ph.nbands = nbands;
   ph.nchunks = nbands * ph.CPB;
-  const int nwg = ph.nchunks / NS;
-  ph.nwg = nwg < 1 ? 1 : (nwg > G ? G : nwg);
+  ph.nunits = whole ? nbands : ph.nchunks;
+  ph.upc = whole ? ph.CPB : 1;
+  if (whole) {
+    const int per = (nbands + G - 1) / G;
+    ph.nwg = (nbands + per - 1) / per;
+  } else {
+    const int nwg = ph.nchunks / NS;
+    ph.nwg = nwg < 1 ? 1 : (nwg > G ? G : nwg);
+  }
   return ph;
 }
 
@@ -1005,15 +1054,18 @@ Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp, int G) {
   p.n_items = p.n_pairs < G ? p.n_pairs : G;
   if (p.n_items > MAX_ITEMS) p.n_items = MAX_ITEMS;
   p.ngroups = mlp ? F / 128 : 0;
-  if (mlp) p.gu = make_phase(KT1, F / 16, P, NS, G);
-  p.dn = make_phase(K2 / 128, N / 32, P, NS, G);
+  // gate/up: whole bands when splitting would give a workgroup fewer than
+  // two bands (then most bands would be shared, and each shared band costs
+  // a round trip through memory at its end)
+  if (mlp) p.gu = make_phase(KT1, F / 16, P, NS, G, F / 16 < 2 * G);
+  p.dn = make_phase(K2 / 128, N / 32, P, NS, G, false);
   p.ok = p.ngroups <= MAX_GROUPS && (!mlp || F / 16 <= MAX_GBANDS) && N / 32 <= CTRL_WORDS - C_DPCNT;
   size_t o = CTRL_BYTES;
   p.off_xa = o;
   o = align256(o + (size_t)M * K1);
   p.off_xs = o;
   o = align256(o + (fmt == FMT_BLOCK ? (size_t)KT1 * p.Mpad * 4 : (size_t)M * (K1 / 32)));
-  const size_t part = (size_t)MAX_WG * 2 * 2 * M * 16 * 4;
+  const size_t part = (size_t)MAX_WG * 2 * 2 * p.Mpad * 16 * 4;  // two slots of [2][Mpad][16] fp32 each
   p.off_a32 = o;
   if (mlp) o = align256(o + (size_t)M * F * 4);
   p.off_aq = o;
