@@ -217,5 +217,8 @@ __device__ __forceinline__ void st_coherent_b128(__amdgpu_buffer_rsrc_t r, uint3
 __device__ __forceinline__ uint32_t ld_coherent_u8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, AUX_SC1);
 }
+__device__ __forceinline__ uint32_t ld_coherent_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX_SC1);
+}
 
 }  // namespace sgd

@@ -117,6 +117,28 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // ---------------------------------------------------------------------------
+// Layout of the fp8 activations the kernel writes to the workspace (Q(x) and
+// Q(a), M rows of K codes): m-tile by m-tile.  m-tile t holds rows
+// 16t..16t+Mt-1 (Mt = min(16, M - 16t)) as K/16 segments of 16 columns, each
+// segment the Mt rows' 16 codes in row order.  The 16 rows x 16 columns one
+// quarter-wavefront of an operand load needs are then 256 contiguous bytes,
+// and one load instruction of a whole wavefront reads 1 KB in one piece
+// (row-major rows K bytes apart would put the 16 rows of every load on 16
+// different cache lines, all in the same L2 channel when K is a multiple of
+// 4 KB).  A 128-column group of an m-tile is 128*Mt contiguous bytes.
+// MX scales alike: m-tile t holds, per 128-column k-tile, the Mt rows' four
+// E8M0 bytes (one dword per row).
+__device__ __forceinline__ uint32_t act_tile_rows(int M, int row) { return (uint32_t)min(16, M - (row & ~15)); }
+__device__ __forceinline__ uint32_t act_code_off(int M, int K, int row, int col) {
+  return (uint32_t)(row & ~15) * (uint32_t)K + (uint32_t)(col >> 4) * 16u * act_tile_rows(M, row) +
+         (uint32_t)(row & 15) * 16u + (uint32_t)(col & 15);
+}
+__device__ __forceinline__ uint32_t act_scale_off(int M, int K, int row, int kt) {
+  return (uint32_t)(row & ~15) * (uint32_t)(K >> 5) + (uint32_t)kt * 4u * act_tile_rows(M, row) +
+         (uint32_t)(row & 15) * 4u;
+}
+
+// ---------------------------------------------------------------------------
 // static schedule
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int range_start(const Phase& ph, int W) {
@@ -189,16 +211,16 @@ __host__ __device__ constexpr int xl_bytes(int fmt, int Mpad, int K1) {
 // words (block: fp32 bits in S0; mx: S0/S1 = dwords holding this lane's two
 // 32-column-block scales for gate/up, its own scale slot for the second
 // GEMM), fp8 activations (one 32-byte operand per m-tile) and their scales
-// (block: rows 4*(l/16)..+3 as v4f; mx: gate/up: this lane's two
-// 32-column-block bytes, second GEMM: its own scale slot in X0).  Each phase
-// has a ring of its own.
+// (block: rows 4*(l/16)..+3 as v4f; mx, in X0: gate/up: the dword of the
+// four 32-column-block scales of this lane's row, second GEMM: this lane's
+// own block scale byte).  Each phase has a ring of its own.
 template <int MT, int P>
 struct Ring {
   v8i RB[P][2];
   uint32_t S0[P][2], S1[P][2];
   v8i RA[P][MT];
   v4f XB[P][MT];
-  uint32_t X0[P][MT], X1[P][MT];
+  uint32_t X0[P][MT];
 };
 
 template <int MT, int FMT, int P, int XL>
@@ -212,8 +234,8 @@ struct Streamer {
   // lane constants
   uint32_t lo16;                   // l * 16
   uint32_t mo_gu0, mo_gu1, mo_dn;  // mx weight-scale lane offsets (bytes)
-  uint32_t xa_lane, aq_lane;       // activation lane offsets (bytes), m-tile 0, k-tile 0
-  uint32_t xs_lane, as_lane;       // activation-scale lane offsets (bytes)
+  uint32_t xsh;                    // mx gate/up: bit offset of this lane's first block scale in X0
+  uint32_t xs_lane;                // block format: activation-scale lane offset (bytes)
   int KdA;                         // row length of the second GEMM's activation
 
   __device__ Streamer(const Args& args, int wq, const uint8_t* lds_x) : a(args), q(wq), lx(lds_x) {
@@ -222,18 +244,10 @@ struct Streamer {
     mo_gu0 = ((uint32_t)(l & 15) + 16u * (uint32_t)((l >> 4) >> 1)) * 4u;
     mo_gu1 = ((uint32_t)(l & 15) + 16u * (2u + (uint32_t)((l >> 4) >> 1))) * 4u;
     mo_dn = (uint32_t)l * 4u;
-    const uint32_t KT1 = (uint32_t)(a.K1 >> 7);
     KdA = a.mlp ? a.F : a.K1;
-    xa_lane = (uint32_t)(l & 15) * (uint32_t)a.K1 + 16u * (uint32_t)(l >> 4);
-    aq_lane = (uint32_t)(l & 15) * (uint32_t)KdA + 16u * (uint32_t)(l >> 4);
-    if (FMT == FMT_BLOCK) {
-      xs_lane = 16u * (uint32_t)(l >> 4);
-      as_lane = 16u * (uint32_t)(l >> 4);
-    } else {
-      // gate/up: blocks (l/16)/2 and 2 + (l/16)/2 of row l%16; second GEMM: block l/16
-      xs_lane = (uint32_t)(l & 15) * (KT1 * 4u) + (uint32_t)((l >> 4) >> 1);
-      as_lane = (uint32_t)(l & 15) * (uint32_t)(KdA >> 5) + (uint32_t)(l >> 4);
-    }
+    // gate/up lanes use blocks (l/16)/2 and 2 + (l/16)/2 of their k-tile
+    xsh = 8u * (uint32_t)((l >> 4) >> 1);
+    xs_lane = 16u * (uint32_t)(l >> 4);
   }
 
   __device__ __forceinline__ void make_resources(bool gu) {
@@ -318,27 +332,27 @@ struct Streamer {
           R.XB[s][mt] = *reinterpret_cast<const v4f*>(sc + (kt * (16 * MT) + 16 * mt + 4 * (l >> 4)) * 4);
         } else {
           const uint8_t* e = sc + (mt * 16 + (l & 15)) * (a.K1 >> 5) + 4 * kt;
-          if (GU) {
-            R.X0[s][mt] = e[(l >> 4) >> 1];
-            R.X1[s][mt] = e[2 + ((l >> 4) >> 1)];
-          } else {
-            R.X0[s][mt] = e[l >> 4];
-          }
+          R.X0[s][mt] = GU ? *reinterpret_cast<const uint32_t*>(e) : (uint32_t)e[l >> 4];
         }
       }
       return;
     }
+    // workspace layout: m-tiles of 16-column segments (act_code_off); lanes
+    // whose row is past M read zeros
+    const uint32_t r = (uint32_t)(lane_id() & 15), g = (uint32_t)(lane_id() >> 4);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint32_t o = ok ? (GU ? xa_lane : aq_lane) + (uint32_t)mt * 16u * Kd + kt * 128u : OOB;
-      R.RA[s][mt] = make_v8i(ld4(rx, o), ld4(rx, ok ? o + 64u : OOB));
+      const int Mt = min(16, a.M - 16 * mt);
+      const bool v = ok && (int)r < Mt;
+      const uint32_t uMt = (uint32_t)max(Mt, 0);
+      const uint32_t o = v ? (uint32_t)mt * 16u * Kd + (kt * 8u + g) * 16u * uMt + r * 16u : OOB;
+      R.RA[s][mt] = make_v8i(ld4(rx, o), ld4(rx, v ? o + 64u * uMt : OOB));
       if (FMT == FMT_BLOCK) {
-        const uint32_t so = (GU ? xs_lane : as_lane) + (kt * (uint32_t)a.Mpad + 16u * (uint32_t)mt) * 4u;
+        const uint32_t so = xs_lane + (kt * (uint32_t)a.Mpad + 16u * (uint32_t)mt) * 4u;
         R.XB[s][mt] = ld_coherent_v4f(rxs, ok ? so : OOB);
       } else {
-        const uint32_t so = (GU ? xs_lane : as_lane) + (uint32_t)mt * 16u * (Kd >> 5) + kt * 4u;
-        R.X0[s][mt] = ld_coherent_u8(rxs, ok ? so : OOB);
-        if (GU) R.X1[s][mt] = ld_coherent_u8(rxs, ok ? so + 2u : OOB);
+        const uint32_t so = (uint32_t)mt * 16u * (Kd >> 5) + kt * 4u * uMt + r * 4u;
+        R.X0[s][mt] = GU ? ld_coherent_u32(rxs, v ? so : OOB) : ld_coherent_u8(rxs, v ? so + g : OOB);
       }
     }
   }
@@ -367,8 +381,8 @@ struct Streamer {
     for (int mt = 0; mt < MT; ++mt) {
       float s0 = 1.0f, s1 = 1.0f;
       if (FMT == FMT_MX) {
-        s0 = pow2_pos((int)R.X0[s][mt] - 127);
-        s1 = pow2_pos((int)R.X1[s][mt] - 127);
+        s0 = pow2_pos((int)((R.X0[s][mt] >> xsh) & 0xFFu) - 127);
+        s1 = pow2_pos((int)((R.X0[s][mt] >> (xsh + 16u)) & 0xFFu) - 127);
       }
       const v8i x = R.RA[s][mt];
       av[mt][0] = widen8((uint32_t)x[0], (uint32_t)x[1], s0);
@@ -657,15 +671,15 @@ __device__ __forceinline__ void xq_item(const Args& a, int item) {
       uint32_t cw[8], se = 0;
       float sf = 1.0f;
       quant_block32<FMT>(v, cw, &sf, &se);
-      const uint32_t off = (uint32_t)row * (uint32_t)a.K1 + (uint32_t)(kg * 128 + 32 * j);
+      const uint32_t off = act_code_off(a.M, a.K1, row, kg * 128 + 32 * j);
       st_coherent_b128(rxa, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
-      st_coherent_b128(rxa, off + 16u, make_uint4(cw[4], cw[5], cw[6], cw[7]));
+      st_coherent_b128(rxa, off + 16u * act_tile_rows(a.M, row), make_uint4(cw[4], cw[5], cw[6], cw[7]));
       if (FMT == FMT_BLOCK) {
         if (j == 0) st_coherent(sbl + row, sf);
       } else {
         const uint32_t e4 = pack4_lanes(se);
         if (j == 0)
-          st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.xs) + (size_t)row * (a.K1 >> 5) + 4 * kg), e4);
+          st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.xs) + act_scale_off(a.M, a.K1, row, kg)), e4);
       }
     }
     if (FMT == FMT_BLOCK && mt == MTa - 1) zero_pad_scales(sbl, a.M, a.Mpad);
@@ -695,15 +709,15 @@ __device__ __forceinline__ void requant_group(const Args& a, int g) {
     uint32_t cw[8], se = 0;
     float sf = 1.0f;
     quant_block32<FMT>(v, cw, &sf, &se);
-    const uint32_t off = (uint32_t)r * (uint32_t)a.F + col;
+    const uint32_t off = act_code_off(a.M, a.F, r, (int)col);
     st_coherent_b128(raq, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
-    st_coherent_b128(raq, off + 16u, make_uint4(cw[4], cw[5], cw[6], cw[7]));
+    st_coherent_b128(raq, off + 16u * act_tile_rows(a.M, r), make_uint4(cw[4], cw[5], cw[6], cw[7]));
     if (FMT == FMT_BLOCK) {
       if (j == 0) st_coherent(static_cast<float*>(a.as) + (size_t)g * a.Mpad + r, sf);
     } else {
       const uint32_t e4 = pack4_lanes(se);
       if (j == 0)
-        st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.as) + (size_t)r * (a.F >> 5) + 4 * g), e4);
+        st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.as) + act_scale_off(a.M, a.F, r, g)), e4);
     }
   }
   if (FMT == FMT_BLOCK) zero_pad_scales(static_cast<float*>(a.as) + (size_t)g * a.Mpad, a.M, a.Mpad);
