@@ -182,7 +182,7 @@ struct Lds {
   uint32_t arrived[NSLOT];         // streaming wavefronts that filled the slot
   uint32_t consumed;               // band events the sync wavefront has taken
   uint32_t xq_ok;                  // Q(x) complete
-  uint32_t dn_ok;                  // the groups of Q(a) this workgroup reads are ready
+  uint32_t rdy[MAX_GROUPS / 32];   // bit g: group g of Q(a) (k-tile g of the second GEMM) is ready
 };
 
 __device__ __forceinline__ uint32_t lds_load(const uint32_t* p) {
@@ -438,6 +438,17 @@ struct Streamer {
     }
   }
 
+  // Wait until the groups of Q(a) that chunk cp reads are ready (its k-tiles
+  // lie in one word of the mask: P divides 32 and k-tiles start at multiples of P).
+  template <int NS, int NSLOT>
+  static __device__ __forceinline__ void wait_groups(Lds<MT, NS, NSLOT>& L, const ChunkPos& cp, int KT) {
+    if (!cp.ok) return;
+    const int n = min(P, KT - cp.kt0);
+    const uint32_t need = ((1u << n) - 1u) << (cp.kt0 & 31);
+    const uint32_t* w = &L.rdy[cp.kt0 >> 5];
+    while ((lds_load(w) & need) != need) __builtin_amdgcn_s_sleep(1);
+  }
+
   // Hand this wavefront's sums for band event k to the sync wavefront.
   template <int NS, int NSLOT>
   __device__ __forceinline__ void publish(Lds<MT, NS, NSLOT>& L, int k, v4f (&acc)[2][MT]) {
@@ -472,8 +483,13 @@ struct Streamer {
 #pragma unroll
     for (int s = 0; s < P; ++s) load_b<GU>(R, s, cp, KT, s);
     between();
-    // activations only once they exist (the LDS copy of Q(x) already does)
-    if (!(XL && (GU || !a.mlp))) lds_wait_geq(GU || !a.mlp ? &L.xq_ok : &L.dn_ok, 1u);
+    // activations only once they exist (the LDS copy of Q(x) already does;
+    // Q(a) chunk by chunk, as its groups become ready)
+    if (GU || !a.mlp) {
+      if (!XL) lds_wait_geq(&L.xq_ok, 1u);
+    } else {
+      wait_groups(L, cp, KT);
+    }
 #pragma unroll
     for (int s = 0; s < P; ++s) load_a<GU>(R, s, cp, KT, s);
     const int bf = c0 / ph.CPB, bl = (c1 - 1) / ph.CPB;
@@ -487,6 +503,7 @@ struct Streamer {
       while (c < hi) {
         const int cn = c + NS;
         const ChunkPos np = chunk_pos<P>(ph, cn, c1);
+        if (!GU && a.mlp) wait_groups(L, np, KT);
 #pragma unroll
         for (int s = 0; s < P; ++s) {
           const int kt = cp.kt0 + s;
@@ -743,6 +760,32 @@ __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Poll the group-ready flags of groups [g0, g1) until all are set, copying
+// each 32-group word into the workgroup's LDS mask as its flags rise (flags
+// only rise during a launch, so every copy only adds bits).
+template <int MT, int NS, int NSLOT>
+__device__ __forceinline__ void mirror_ready(Lds<MT, NS, NSLOT>& L, const uint32_t* flags, int g0, int g1) {
+  const int l = lane_id();
+  const int a0 = g0 & ~31;
+  for (;;) {
+    bool all = true;
+    for (int i0 = a0; i0 < g1; i0 += 64) {
+      const int i = i0 + l;
+      const bool in = i >= g0 && i < g1;
+      const bool r = in && load_agent(flags + i) != 0u;
+      const uint64_t bal = __ballot(r);
+      all = all && __all(r || !in);
+      if (l == 0) {
+        lds_store(&L.rdy[i0 >> 5], (uint32_t)bal);
+        if (i0 + 32 < g1) lds_store(&L.rdy[(i0 >> 5) + 1], (uint32_t)(bal >> 32));
+      }
+    }
+    if (all) break;
+    __builtin_amdgcn_s_sleep(4);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Split-K partials of shared bands, slot (workgroup W, side).  Up to two row
 // tiles: [2][M][16] fp32, rows < M only (one row costs two stores).  More:
 // the sync wavefront's sums in their register layout, [2][MT][64 lanes] x
@@ -937,8 +980,7 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L) 
           g0 = (c0 % ph.CPB) * Cfg<MT>::P;
           g1 = min(ph.KT, ((c1 - 1) % ph.CPB) * Cfg<MT>::P + Cfg<MT>::P);
         }
-        wait_flags(page + PG_RDY + g0, g1 - g0);
-        if (l == 0) lds_store(&L.dn_ok, 1u);
+        mirror_ready(L, page + PG_RDY, g0, g1);
       }
       for (int b = c0 / ph.CPB; b <= (c1 - 1) / ph.CPB; ++b) {
         v4f s[2][MT];
@@ -980,7 +1022,7 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     for (int i = 0; i < C::NSLOT; ++i) L.arrived[i] = 0u;
     L.consumed = 0u;
     L.xq_ok = XL ? 1u : 0u;
-    L.dn_ok = 0u;
+    for (int i = 0; i < MAX_GROUPS / 32; ++i) L.rdy[i] = 0u;
   }
   __syncthreads();
   if (wv == 0) {
@@ -1053,6 +1095,17 @@ Phase make_phase(int KT, int nbands, int P, int NS, int G, bool whole) {
   } else {
     const int nwg = ph.nchunks / NS;
     ph.nwg = nwg < 1 ? 1 : (nwg > G ? G : nwg);
+    // Rather S workgroups per band (ranges that never straddle a band: one
+    // band event, one split-K combine, and only that band's k-range of Q(a)
+    // to wait for), for the smallest S that needs fewer rounds of chunks per
+    // streaming wavefront than the plain split.
+    const int rounds = ((ph.nchunks + ph.nwg - 1) / ph.nwg + NS - 1) / NS;
+    for (int S = 1; S <= G / nbands && S <= ph.CPB; ++S) {
+      if (((ph.CPB + S - 1) / S + NS - 1) / NS < rounds) {
+        ph.nwg = nbands * S;
+        break;
+      }
+    }
   }
   return ph;
 }
