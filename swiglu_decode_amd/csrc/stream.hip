@@ -704,37 +704,49 @@ __device__ __forceinline__ void xq_item(const Args& a, int item) {
 }
 
 // Re-quantize 128-column group g of a = silu(g)*u (fp32, written by other
-// workgroups: read agent-coherently), one lane per (row, 32-column block).
-template <int FMT>
+// workgroups: read agent-coherently), one lane per (row, 32-column block),
+// U blocks per lane at a time with all their loads issued first (one memory
+// round trip per U blocks).
+template <int FMT, int U>
 __device__ __forceinline__ void requant_group(const Args& a, int g) {
   const int l = lane_id();
   const __amdgpu_buffer_rsrc_t r32 = make_rsrc(a.a32, (uint32_t)a.M * (uint32_t)a.F * 4u);
   const __amdgpu_buffer_rsrc_t raq = make_rsrc(a.aq, (uint32_t)a.M * (uint32_t)a.F);
-  for (int i = l; i < a.M * 4; i += 64) {  // (M*4 is a multiple of 4: the 4 lanes of a row agree)
-    const int r = i >> 2, j = i & 3;
-    const uint32_t col = (uint32_t)(g * 128 + 32 * j);
-    const uint32_t base = ((uint32_t)r * (uint32_t)a.F + col) * 4u;
-    float v[32];
+  const int n = a.M * 4;  // (a multiple of 4: the 4 lanes of a row agree on i < n)
+  for (int i0 = l; i0 < n; i0 += 64 * U) {
+    float vv[U][32];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const v4f t = ld_coherent_v4f(r32, base + 16u * c);
-      v[4 * c] = t[0];
-      v[4 * c + 1] = t[1];
-      v[4 * c + 2] = t[2];
-      v[4 * c + 3] = t[3];
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 64 * u;
+      const uint32_t base = ((uint32_t)(i >> 2) * (uint32_t)a.F + (uint32_t)(g * 128 + 32 * (i & 3))) * 4u;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const v4f t = ld_coherent_v4f(r32, i < n ? base + 16u * c : OOB);
+        vv[u][4 * c] = t[0];
+        vv[u][4 * c + 1] = t[1];
+        vv[u][4 * c + 2] = t[2];
+        vv[u][4 * c + 3] = t[3];
+      }
     }
-    uint32_t cw[8], se = 0;
-    float sf = 1.0f;
-    quant_block32<FMT>(v, cw, &sf, &se);
-    const uint32_t off = act_code_off(a.M, a.F, r, (int)col);
-    st_coherent_b128(raq, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
-    st_coherent_b128(raq, off + 16u * act_tile_rows(a.M, r), make_uint4(cw[4], cw[5], cw[6], cw[7]));
-    if (FMT == FMT_BLOCK) {
-      if (j == 0) st_coherent(static_cast<float*>(a.as) + (size_t)g * a.Mpad + r, sf);
-    } else {
-      const uint32_t e4 = pack4_lanes(se);
-      if (j == 0)
-        st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.as) + act_scale_off(a.M, a.F, r, g)), e4);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 64 * u;
+      if (i >= n) break;
+      const int r = i >> 2, j = i & 3;
+      const uint32_t col = (uint32_t)(g * 128 + 32 * j);
+      uint32_t cw[8], se = 0;
+      float sf = 1.0f;
+      quant_block32<FMT>(vv[u], cw, &sf, &se);
+      const uint32_t off = act_code_off(a.M, a.F, r, (int)col);
+      st_coherent_b128(raq, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
+      st_coherent_b128(raq, off + 16u * act_tile_rows(a.M, r), make_uint4(cw[4], cw[5], cw[6], cw[7]));
+      if (FMT == FMT_BLOCK) {
+        if (j == 0) st_coherent(static_cast<float*>(a.as) + (size_t)g * a.Mpad + r, sf);
+      } else {
+        const uint32_t e4 = pack4_lanes(se);
+        if (j == 0)
+          st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.as) + act_scale_off(a.M, a.F, r, g)), e4);
+      }
     }
   }
   if (FMT == FMT_BLOCK) zero_pad_scales(static_cast<float*>(a.as) + (size_t)g * a.Mpad, a.M, a.Mpad);
@@ -915,7 +927,9 @@ __device__ __forceinline__ void finish_gu_band(const Args& a, int b, v4f (&s)[2]
   if (l == 0) old = atomic_add_agent(&a.ctrl[C_GCNT + grp], 1u);
   if (uni((int)old) != 7) return;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  requant_group<FMT>(a, grp);
+  // (MX: several blocks per lane at a time; the block format measured
+  // faster with one)
+  requant_group<FMT, (FMT == FMT_MX ? (MT < 4 ? MT : 4) : 1)>(a, grp);
   drain_memory();
   raise_flag(a.ctrl, PG_RDY, grp);
 }
