@@ -14,6 +14,8 @@ bf16 x + bf16 y; intermediates and activation scales are not counted.
 Output: one JSON line (see the keys below).  `value` is the step's aggregate
 algorithmic bytes divided by its time, in GB/s.  `roofline` describes the
 M=16 launch (the ≥70 %-of-peak target case); `per_m` lists every M.
+`read_stream_ceiling` is the rate of a plain streaming read on the same GPU,
+reported as context (the roofline peak stays the nominal 8 TB/s).
 `cpu_baseline` times the CPU oracle on a bounded sample on this host; the
 same oracle outputs are compared with the GPU outputs (`parity`).
 """
@@ -56,6 +58,32 @@ def read_traffic():
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_ceiling(dev, nbytes=4 << 30, reps=10):
+    """Attainable HBM read rate on this GPU, for context: the library's plain
+    streaming-read kernel over `nbytes` of device memory, timed with HIP
+    events on the launch stream."""
+    import torch
+    import swiglu_decode_amd as sgd
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        sink = torch.empty((1,), dtype=torch.int32, device=dev)
+        for _ in range(2):
+            sgd.read_stream(t, sink)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            sgd.read_stream(t, sink)
+        e1.record(stream)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del t
+    torch.cuda.empty_cache()
+    return dict(gbs=round(nbytes / us / 1e3, 1), kernel=f"sgd_read_stream over {nbytes >> 20} MiB",
+                pct_of_peak=round(100.0 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1))
 
 
 def algorithmic_bytes(M, d, F, scale_bytes):
@@ -169,6 +197,8 @@ def main():
                 algorithmic_bytes_per_launch=per_m[rm]["bytes"],
                 traffic_bytes_per_launch=int(tb) if tb else None)
 
+    ceiling = read_ceiling(dev)
+
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
@@ -193,6 +223,7 @@ def main():
                    "parallelism": "single GPU"},
         "per_m": {str(m): per_m[m] for m in ms},
         "roofline": roof,
+        "read_stream_ceiling": ceiling,
         "cpu_baseline": cpu,
         "parity": parity,
     }
@@ -200,11 +231,12 @@ def main():
 
 
 def cpu_baseline(inp, ms, fmt, y_out, step_bytes):
-    """Time the CPU oracle (as it stands) on a bounded sample: one MLP call at
-    M=1 and one at M=16 on the same workload, weights quantized beforehand
-    (the analogue of the offline pack, untimed).  Returns the baseline in the
-    bench's unit (algorithmic GB/s) and the GPU-vs-oracle parity of those
-    calls."""
+    """Time the CPU oracle (as it stands) on a bounded sample: passes of one
+    MLP call at M=1 and one at M=16 on the same workload, repeated until about
+    10 s of CPU time have passed (at most 12 passes), weights quantized
+    beforehand (the analogue of the offline pack, untimed).  Returns the
+    baseline in the bench's unit (algorithmic GB/s) and the GPU-vs-oracle
+    parity of those calls."""
     import numpy as np
     from oracle import ref
     from synth import bf16_to_f64
@@ -219,18 +251,22 @@ def cpu_baseline(inp, ms, fmt, y_out, step_bytes):
     F = q[0].N
     scale_bytes = sum(int(np.asarray(w.scales).nbytes) for w in q)
     sample = [m for m in (1, 16) if m in ms] or [ms[0]]
-    t_tot, b_tot = 0.0, 0
+    t_tot, b_tot, passes = 0.0, 0, 0
     parity = {}
-    for m in sample:
-        t0 = time.perf_counter()
-        y = ref.swiglu_mlp(x[:m], *q)
-        t_tot += time.perf_counter() - t0
-        b_tot += algorithmic_bytes(m, d, F, scale_bytes)
-        parity[str(m)] = dict(rel_fro=float(f"{ref.rel_fro(y_out[m], y):.3e}"),
-                              max_abs_ratio=float(f"{ref.max_abs_ratio(y_out[m], y):.3e}"))
+    while passes < 12 and (passes == 0 or t_tot < 10.0):
+        for m in sample:
+            t0 = time.perf_counter()
+            y = ref.swiglu_mlp(x[:m], *q)
+            t_tot += time.perf_counter() - t0
+            b_tot += algorithmic_bytes(m, d, F, scale_bytes)
+            if passes == 0:
+                parity[str(m)] = dict(rel_fro=float(f"{ref.rel_fro(y_out[m], y):.3e}"),
+                                      max_abs_ratio=float(f"{ref.max_abs_ratio(y_out[m], y):.3e}"))
+        passes += 1
     cpu = dict(value=round(b_tot / t_tot / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
-               sample=f"one oracle MLP call at M={sample} (x quantization, fp64 dequantize + matmuls, "
-                      f"SwiGLU, re-quantization), weights pre-quantized; {t_tot:.1f} s on this host")
+               sample=f"{passes} pass(es) of one oracle MLP call at each M in {sample} (x quantization, "
+                      f"fp64 dequantize + matmuls, SwiGLU, re-quantization), weights pre-quantized; "
+                      f"{t_tot:.1f} s on this host")
     return cpu, parity
 
 

@@ -210,6 +210,18 @@ int sgd_head_logits(const float* h, int M, int K, const uint16_t* w_bf16, int N,
 /* out[m] = argmax_n logits[m, n] (lowest index among equal maxima). */
 int sgd_argmax_rows(const float* logits, int M, int N, int32_t* out, void* stream);
 
+/* ---- measurement aid ---------------------------------------------------- */
+/*
+ * Read `bytes` bytes of device memory at `buf` once, as a plain streaming
+ * read (16-byte loads, grid-stride, 8192 workgroups of 256 threads), and
+ * write nothing but possibly the one word at `sink` (device, caller-owned).
+ * Timing it gives the attainable HBM read rate of the device, the context
+ * for the hot path's achieved rates (a weight stream is a read stream).
+ * buf 16-byte aligned, bytes a multiple of 16, sink 4-byte aligned.
+ * Errors: SGD_EINVAL (null pointer, bytes == 0), SGD_EALIGN.
+ */
+int sgd_read_stream(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -258,3 +258,18 @@ def argmax_rows(logits, out=None):
     _need(out, "out", torch.int32, (M,), logits.device)
     _lib.check("sgd_argmax_rows", lib().sgd_argmax_rows(_ptr(logits), M, N, _ptr(out), _stream(logits)))
     return out
+
+
+def read_stream(buf, sink=None):
+    """One plain streaming read of the bytes of `buf` (a contiguous CUDA
+    tensor whose size is a multiple of 16 bytes): a measurement aid for the
+    attainable HBM read rate.  `sink` is a one-element int32 tensor the
+    kernel may write (allocated here when not given)."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous CUDA tensor")
+    if sink is None:
+        sink = torch.empty((1,), dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", torch.int32, (1,), buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _lib.check("sgd_read_stream", lib().sgd_read_stream(_ptr(buf), nbytes, _ptr(sink), _stream(buf)))
+    return sink

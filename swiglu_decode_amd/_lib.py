@@ -52,6 +52,7 @@ SIGNATURES = {
     "sgd_residual_add": (_i, [_vp, _vp, _i, _i, _vp]),
     "sgd_head_logits": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
     "sgd_argmax_rows": (_i, [_vp, _i, _i, _vp, _vp]),
+    "sgd_read_stream": (_i, [_vp, _sz, _vp, _vp]),
 }
 
 _LIB = None

@@ -111,6 +111,12 @@ int sgd_workspace_clear(void* workspace, size_t bytes, void* stream) {
   return launch_fill_zero(workspace, bytes, as_stream(stream));
 }
 
+int sgd_read_stream(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes == 0) return SGD_EINVAL;
+  if (!al16(buf) || (bytes % 16) || (reinterpret_cast<uintptr_t>(sink) & 3)) return SGD_EALIGN;
+  return launch_read_stream(buf, bytes, sink, as_stream(stream));
+}
+
 int sgd_scaled_gemm(const uint16_t* x_bf16, int M, const sgd_weight* w, uint16_t* y_bf16,
                     void* workspace, size_t ws_bytes, void* stream) {
   int rc = check_weight(w);

@@ -17,6 +17,7 @@ int launch_unpack_weight(int fmt, const uint8_t* codes, const void* scales, int 
 int launch_quantize_act(int fmt, const uint16_t* x, int M, int K, uint8_t* codes, void* scales,
                         hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+int launch_read_stream(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // Streaming GEMM / fused MLP.  `gate`/`up` are null for the plain GEMM.
 struct Problem {

@@ -109,6 +109,12 @@ def test_argument_errors_launch_nothing(L):
     assert L.sgd_head_logits(P(0x1000), 200, 256, P(0x1000), 256, P(0x1000), None) == E["EINVAL"]
     assert L.sgd_argmax_rows(P(0x1000), 0, 10, P(0x1000), None) == E["EINVAL"]
     assert L.sgd_workspace_clear(P(0x1000), 24, None) == E["EALIGN"]
+    # measurement aid
+    assert L.sgd_read_stream(None, 1024, P(0x1000), None) == E["EINVAL"]
+    assert L.sgd_read_stream(P(0x1000), 1024, None, None) == E["EINVAL"]
+    assert L.sgd_read_stream(P(0x1000), 1000, P(0x1000), None) == E["EALIGN"]
+    assert L.sgd_read_stream(P(0x1008), 1024, P(0x1000), None) == E["EALIGN"]
+    assert L.sgd_read_stream(P(0x1000), 1024, P(0x1002), None) == E["EALIGN"]
 
 
 def test_binding_refuses_wrong_dtypes_without_gpu():

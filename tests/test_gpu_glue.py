@@ -69,3 +69,16 @@ def test_argmax_rows_ties_take_lowest_index():
     am = sgd.argmax_rows(torch.from_numpy(lg).to(d))
     torch.cuda.synchronize()
     assert np.array_equal(am.cpu().numpy(), ref.argmax_rows(lg))
+
+
+def test_read_stream_runs_and_writes_nothing_but_the_sink():
+    """The measurement aid reads its buffer and leaves it untouched."""
+    d = dev()
+    buf = torch.arange(1 << 20, dtype=torch.int32, device=d)
+    ref_copy = buf.clone()
+    sink = torch.full((1,), 7, dtype=torch.int32, device=d)
+    sgd.read_stream(buf, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref_copy)
+    with pytest.raises(Exception):
+        sgd.read_stream(buf[1:])  # 4 bytes off the 16-byte alignment
