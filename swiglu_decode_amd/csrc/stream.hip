@@ -58,6 +58,11 @@ struct Cfg {
   static constexpr int P = (MT == 2 || MT >= 8) ? 2 : 4;
   static constexpr int NSLOT = 2;
   static constexpr int NWAVE = NS + 1;
+  // ring slots (= k-tiles per chunk) of the MLP's second GEMM (deeper rings,
+  // that would prefetch a workgroup's whole share of it while Q(a) is not
+  // ready, measured slower: their traffic competes with the last gate/up
+  // loads, which are on the critical path)
+  static constexpr int PD = P;
 };
 
 struct Phase {
@@ -214,6 +219,10 @@ __host__ __device__ constexpr int xl_bytes(int fmt, int Mpad, int K1) {
 // (block: rows 4*(l/16)..+3 as v4f; mx, in X0: gate/up: the dword of the
 // four 32-column-block scales of this lane's row, second GEMM: this lane's
 // own block scale byte).  Each phase has a ring of its own.
+// The three phases a streaming wavefront runs: the MLP's gate/up product,
+// the MLP's second GEMM (activations: Q(a)), and the plain GEMM (Q(x)).
+constexpr int PK_GU = 0, PK_DN = 1, PK_GEMM = 2;
+
 template <int MT, int P>
 struct Ring {
   v8i RB[P][2];
@@ -225,7 +234,6 @@ struct Ring {
 
 template <int MT, int FMT, int P, int XL>
 struct Streamer {
-  using R_t = Ring<MT, P>;
   const Args& a;
   const int q;  // index among the workgroup's streaming wavefronts
   const uint8_t* lx;  // LDS copy of Q(x) (XL)
@@ -236,7 +244,6 @@ struct Streamer {
   uint32_t mo_gu0, mo_gu1, mo_dn;  // mx weight-scale lane offsets (bytes)
   uint32_t xsh;                    // mx gate/up: bit offset of this lane's first block scale in X0
   uint32_t xs_lane;                // block format: activation-scale lane offset (bytes)
-  int KdA;                         // row length of the second GEMM's activation
 
   __device__ Streamer(const Args& args, int wq, const uint8_t* lds_x) : a(args), q(wq), lx(lds_x) {
     const int l = lane_id();
@@ -244,13 +251,14 @@ struct Streamer {
     mo_gu0 = ((uint32_t)(l & 15) + 16u * (uint32_t)((l >> 4) >> 1)) * 4u;
     mo_gu1 = ((uint32_t)(l & 15) + 16u * (2u + (uint32_t)((l >> 4) >> 1))) * 4u;
     mo_dn = (uint32_t)l * 4u;
-    KdA = a.mlp ? a.F : a.K1;
     // gate/up lanes use blocks (l/16)/2 and 2 + (l/16)/2 of their k-tile
     xsh = 8u * (uint32_t)((l >> 4) >> 1);
     xs_lane = 16u * (uint32_t)(l >> 4);
   }
 
-  __device__ __forceinline__ void make_resources(bool gu) {
+  template <int PK>
+  __device__ __forceinline__ void make_resources() {
+    const bool gu = PK == PK_GU;
     const uint32_t KT1 = (uint32_t)(a.K1 >> 7);
     const uint32_t xs_bytes = FMT == FMT_BLOCK ? KT1 * (uint32_t)a.Mpad * 4u : (uint32_t)a.M * (KT1 * 4u);
     if (gu) {
@@ -264,7 +272,7 @@ struct Streamer {
     } else {
       rw0 = rw1 = make_rsrc(a.w2, (uint32_t)a.N * (uint32_t)a.K2);
       rs0 = rs1 = make_rsrc(a.s2, a.scale_bytes_2);
-      if (a.mlp) {
+      if (PK == PK_DN) {
         rx = make_rsrc(a.aq, (uint32_t)a.M * (uint32_t)a.F);
         rxs = make_rsrc(a.as, FMT == FMT_BLOCK ? (uint32_t)(a.F >> 7) * (uint32_t)a.Mpad * 4u
                                               : (uint32_t)a.M * (uint32_t)(a.F >> 5));
@@ -280,8 +288,8 @@ struct Streamer {
   }
 
   // ---- loads of one ring slot (unconditional: fillers read past the end) ----
-  template <bool GU>
-  __device__ __forceinline__ void load_b(R_t& R, int s, const ChunkPos& cp, int KT, int k) {
+  template <bool GU, int PP>
+  __device__ __forceinline__ void load_b(Ring<MT, PP>& R, int s, const ChunkPos& cp, int KT, int k) {
     const int kt_ = cp.kt0 + k;
     const bool ok = cp.ok && kt_ < KT;
     const uint32_t kt = ok ? (uint32_t)kt_ : 0u;
@@ -313,13 +321,14 @@ struct Streamer {
     }
   }
 
-  template <bool GU>
-  __device__ __forceinline__ void load_a(R_t& R, int s, const ChunkPos& cp, int KT, int k) {
+  template <int PK, int PP>
+  __device__ __forceinline__ void load_a(Ring<MT, PP>& R, int s, const ChunkPos& cp, int KT, int k) {
+    constexpr bool GU = PK == PK_GU;
     const int kt_ = cp.kt0 + k;
     const bool ok = cp.ok && kt_ < KT;
     const uint32_t kt = ok ? (uint32_t)kt_ : 0u;
-    const uint32_t Kd = GU ? (uint32_t)a.K1 : (uint32_t)KdA;
-    if (XL && (GU || !a.mlp)) {
+    const uint32_t Kd = PK == PK_DN ? (uint32_t)a.F : (uint32_t)a.K1;
+    if (XL && PK != PK_DN) {
       // Q(x) from LDS (fillers read k-tile 0 and are never used)
       const int l = lane_id();
       const int rs = xl_row_stride(a.K1);
@@ -374,17 +383,18 @@ struct Streamer {
   // ~13 bits below the largest product of a group (measured on gfx950); that
   // ~1e-5 relative error would flip fp8 codes of the re-quantized product,
   // while the bf16 instruction's sums are fp32-accurate.
-  __device__ __forceinline__ void step_gu(R_t& R, int s, int kt, v4f (&acc)[2][MT]) {
+  template <int PP>
+  __device__ __forceinline__ void step_gu(Ring<MT, PP>& R, int s, int sa, int kt, v4f (&acc)[2][MT]) {
     const int sh = 8 * (kt & 3);
     v8bf av[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       float s0 = 1.0f, s1 = 1.0f;
       if (FMT == FMT_MX) {
-        s0 = pow2_pos((int)((R.X0[s][mt] >> xsh) & 0xFFu) - 127);
-        s1 = pow2_pos((int)((R.X0[s][mt] >> (xsh + 16u)) & 0xFFu) - 127);
+        s0 = pow2_pos((int)((R.X0[sa][mt] >> xsh) & 0xFFu) - 127);
+        s1 = pow2_pos((int)((R.X0[sa][mt] >> (xsh + 16u)) & 0xFFu) - 127);
       }
-      const v8i x = R.RA[s][mt];
+      const v8i x = R.RA[sa][mt];
       av[mt][0] = widen8((uint32_t)x[0], (uint32_t)x[1], s0);
       av[mt][1] = widen8((uint32_t)x[2], (uint32_t)x[3], s0);
       av[mt][2] = widen8((uint32_t)x[4], (uint32_t)x[5], s1);
@@ -409,7 +419,7 @@ struct Streamer {
           v4f t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[i], t, 0, 0, 0);
-          acc[nb][mt] += t * (R.XB[s][mt] * __uint_as_float(R.S0[s][nb]));
+          acc[nb][mt] += t * (R.XB[sa][mt] * __uint_as_float(R.S0[s][nb]));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -420,30 +430,31 @@ struct Streamer {
   }
 
   // Second GEMM: scaled fp8 MFMA (MX scales in the instruction).
-  __device__ __forceinline__ void step_dn(R_t& R, int s, int kt, v4f (&acc)[2][MT]) {
+  template <int PP>
+  __device__ __forceinline__ void step_dn(Ring<MT, PP>& R, int s, int sa, int kt, v4f (&acc)[2][MT]) {
     const int sh = 8 * (kt & 3);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const v8i av = R.RA[s][mt];
+        const v8i av = R.RA[sa][mt];
         if (FMT == FMT_BLOCK) {
           const v4f z = {0.f, 0.f, 0.f, 0.f};
           const v4f t = mfma_f8(av, R.RB[s][nb], z, 127, 127);
-          acc[nb][mt] += t * (R.XB[s][mt] * __uint_as_float(R.S0[s][nb]));
+          acc[nb][mt] += t * (R.XB[sa][mt] * __uint_as_float(R.S0[s][nb]));
         } else {
-          acc[nb][mt] = mfma_f8(av, R.RB[s][nb], acc[nb][mt], (int)R.X0[s][mt], (int)(R.S0[s][nb] >> sh));
+          acc[nb][mt] = mfma_f8(av, R.RB[s][nb], acc[nb][mt], (int)R.X0[sa][mt], (int)(R.S0[s][nb] >> sh));
         }
       }
     }
   }
 
   // Wait until the groups of Q(a) that chunk cp reads are ready (its k-tiles
-  // lie in one word of the mask: P divides 32 and k-tiles start at multiples of P).
-  template <int NS, int NSLOT>
+  // lie in one word of the mask: PP divides 32 and k-tiles start at multiples of PP).
+  template <int PP, int NS, int NSLOT>
   static __device__ __forceinline__ void wait_groups(Lds<MT, NS, NSLOT>& L, const ChunkPos& cp, int KT) {
     if (!cp.ok) return;
-    const int n = min(P, KT - cp.kt0);
+    const int n = min(PP, KT - cp.kt0);
     const uint32_t need = ((1u << n) - 1u) << (cp.kt0 & 31);
     const uint32_t* w = &L.rdy[cp.kt0 >> 5];
     while ((lds_load(w) & need) != need) __builtin_amdgcn_s_sleep(1);
@@ -466,8 +477,9 @@ struct Streamer {
   // weights of this wavefront's first chunk before `between()` runs (the
   // workgroup-wide x quantization, when there is one; every wavefront calls
   // it exactly once), and with activations after it.
-  template <bool GU, int NS, int NSLOT, class Between>
+  template <int PK, int PP, int NS, int NSLOT, class Between>
   __device__ __forceinline__ void run_phase(Lds<MT, NS, NSLOT>& L, int& k, Between between) {
+    constexpr bool GU = PK == PK_GU;
     const Phase& ph = GU ? a.gu : a.dn;
     const int W = blockIdx.x;
     if (!(W < ph.nwg && range_start(ph, W) < range_start(ph, W + 1))) {
@@ -477,21 +489,21 @@ struct Streamer {
     const int c0 = range_start(ph, W), c1 = range_start(ph, W + 1);
     const int KT = ph.KT;
     int c = c0 + q;
-    make_resources(GU);
-    R_t R;
-    ChunkPos cp = chunk_pos<P>(ph, c, c1);
+    make_resources<PK>();
+    Ring<MT, PP> R;
+    ChunkPos cp = chunk_pos<PP>(ph, c, c1);
 #pragma unroll
-    for (int s = 0; s < P; ++s) load_b<GU>(R, s, cp, KT, s);
+    for (int s = 0; s < PP; ++s) load_b<GU>(R, s, cp, KT, s);
     between();
     // activations only once they exist (the LDS copy of Q(x) already does;
     // Q(a) chunk by chunk, as its groups become ready)
-    if (GU || !a.mlp) {
+    if (PK != PK_DN) {
       if (!XL) lds_wait_geq(&L.xq_ok, 1u);
     } else {
-      wait_groups(L, cp, KT);
+      wait_groups<PP>(L, cp, KT);
     }
 #pragma unroll
-    for (int s = 0; s < P; ++s) load_a<GU>(R, s, cp, KT, s);
+    for (int s = 0; s < PP; ++s) load_a<PK>(R, s, cp, KT, s);
     const int bf = c0 / ph.CPB, bl = (c1 - 1) / ph.CPB;
     for (int b = bf; b <= bl; ++b) {
       const int hi = min(c1, (b + 1) * ph.CPB);
@@ -502,19 +514,19 @@ struct Streamer {
         for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
       while (c < hi) {
         const int cn = c + NS;
-        const ChunkPos np = chunk_pos<P>(ph, cn, c1);
-        if (!GU && a.mlp) wait_groups(L, np, KT);
+        const ChunkPos np = chunk_pos<PP>(ph, cn, c1);
+        if (PK == PK_DN) wait_groups<PP>(L, np, KT);
 #pragma unroll
-        for (int s = 0; s < P; ++s) {
+        for (int s = 0; s < PP; ++s) {
           const int kt = cp.kt0 + s;
           if (kt < KT) {
             if (GU)
-              step_gu(R, s, kt, acc);
+              step_gu(R, s, s, kt, acc);
             else
-              step_dn(R, s, kt, acc);
+              step_dn(R, s, s, kt, acc);
           }
           load_b<GU>(R, s, np, KT, s);
-          load_a<GU>(R, s, np, KT, s);
+          load_a<PK>(R, s, np, KT, s);
         }
         c = cn;
         cp = np;
@@ -991,8 +1003,8 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L) 
         // groups (k-tiles of the second GEMM) this workgroup's chunks read
         int g0 = 0, g1 = ph.KT;
         if (c0 / ph.CPB == (c1 - 1) / ph.CPB) {
-          g0 = (c0 % ph.CPB) * Cfg<MT>::P;
-          g1 = min(ph.KT, ((c1 - 1) % ph.CPB) * Cfg<MT>::P + Cfg<MT>::P);
+          g0 = (c0 % ph.CPB) * Cfg<MT>::PD;
+          g1 = min(ph.KT, ((c1 - 1) % ph.CPB) * Cfg<MT>::PD + Cfg<MT>::PD);
         }
         mirror_ready(L, page + PG_RDY, g0, g1);
       }
@@ -1026,7 +1038,9 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L) 
 // ---------------------------------------------------------------------------
 // XL: Q(x) is built in LDS by every workgroup (no cross-workgroup wait
 // before the first product); otherwise it is built once in the workspace.
-template <int MT, int FMT, int XL>
+// MLP: the fused MLP (else the plain GEMM); separate kernels, so that each
+// gets its own register allocation.
+template <int MT, int FMT, int XL, int MLP>
 __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) {
   using C = Cfg<MT>;
   __shared__ Lds<MT, C::NS, C::NSLOT> L;
@@ -1065,11 +1079,11 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
       }
     };
     auto nothing = []() {};
-    if (a.mlp) {
-      st.template run_phase<true>(L, k, quantize_x);
-      st.template run_phase<false>(L, k, nothing);
+    if (MLP) {
+      st.template run_phase<PK_GU, C::P>(L, k, quantize_x);
+      st.template run_phase<PK_DN, C::PD>(L, k, nothing);
     } else {
-      st.template run_phase<false>(L, k, quantize_x);
+      st.template run_phase<PK_GEMM, C::P>(L, k, quantize_x);
     }
   }
 }
@@ -1090,6 +1104,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 int mt_for(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
 int cfg_ns(int MT) { return MT == 1 ? Cfg<1>::NS : MT == 2 ? Cfg<2>::NS : MT == 4 ? Cfg<4>::NS : Cfg<8>::NS; }
 int cfg_p(int MT) { return MT == 1 ? Cfg<1>::P : MT == 2 ? Cfg<2>::P : MT == 4 ? Cfg<4>::P : Cfg<8>::P; }
+int cfg_pd(int MT) { return MT == 1 ? Cfg<1>::PD : MT == 2 ? Cfg<2>::PD : MT == 4 ? Cfg<4>::PD : Cfg<8>::PD; }
 int cfg_nwave(int MT) { return cfg_ns(MT) + 1; }
 
 // Chunks are dealt in equal contiguous ranges: of whole bands when `whole`
@@ -1139,7 +1154,7 @@ Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp, int G) {
   // two bands (then most bands would be shared, and each shared band costs
   // a round trip through memory at its end)
   if (mlp) p.gu = make_phase(KT1, F / 16, P, NS, G, F / 16 < 2 * G);
-  p.dn = make_phase(K2 / 128, N / 32, P, NS, G, false);
+  p.dn = make_phase(K2 / 128, N / 32, mlp ? cfg_pd(p.MT) : P, NS, G, false);
   p.ok = p.ngroups <= MAX_GROUPS && (!mlp || F / 16 <= MAX_GBANDS) && N / 32 <= CTRL_WORDS - C_DPCNT;
   size_t o = CTRL_BYTES;
   p.off_xa = o;
@@ -1161,27 +1176,31 @@ Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp, int G) {
   return p;
 }
 
-template <int MT, int FMT, int XL>
-const void* kernel_ptr() { return reinterpret_cast<const void*>(&stream_kernel<MT, FMT, XL>); }
+template <int MT, int FMT, int XL, int MLP>
+const void* kernel_ptr() { return reinterpret_cast<const void*>(&stream_kernel<MT, FMT, XL, MLP>); }
 
-// Kernel variants: (MT, XL) in (1,0) (1,1) (2,0) (2,1) (4,0) (8,0).
-constexpr int NVAR = 6;
-int var_index(int MT, int XL) { return MT == 1 ? XL : MT == 2 ? 2 + XL : MT == 4 ? 4 : 5; }
+// Kernel variants: (MT, XL) in (1,0) (1,1) (2,0) (2,1) (4,0) (8,0), each for
+// the MLP and for the plain GEMM.
+constexpr int NVAR = 12;
+int var_index(int MT, int XL, bool mlp) {
+  return (MT == 1 ? XL : MT == 2 ? 2 + XL : MT == 4 ? 4 : 5) + (mlp ? 6 : 0);
+}
 
-template <int FMT>
+template <int FMT, int MLP>
 const void* pick_fmt(int vi) {
-  switch (vi) {
-    case 0: return kernel_ptr<1, FMT, 0>();
-    case 1: return kernel_ptr<1, FMT, 1>();
-    case 2: return kernel_ptr<2, FMT, 0>();
-    case 3: return kernel_ptr<2, FMT, 1>();
-    case 4: return kernel_ptr<4, FMT, 0>();
-    default: return kernel_ptr<8, FMT, 0>();
+  switch (vi % 6) {
+    case 0: return kernel_ptr<1, FMT, 0, MLP>();
+    case 1: return kernel_ptr<1, FMT, 1, MLP>();
+    case 2: return kernel_ptr<2, FMT, 0, MLP>();
+    case 3: return kernel_ptr<2, FMT, 1, MLP>();
+    case 4: return kernel_ptr<4, FMT, 0, MLP>();
+    default: return kernel_ptr<8, FMT, 0, MLP>();
   }
 }
-const void* pick_kernel(int MT, int fmt, int XL) {
-  const int vi = var_index(MT, XL);
-  return fmt == FMT_BLOCK ? pick_fmt<FMT_BLOCK>(vi) : pick_fmt<FMT_MX>(vi);
+const void* pick_kernel(int MT, int fmt, int XL, bool mlp) {
+  const int vi = var_index(MT, XL, mlp);
+  if (fmt == FMT_BLOCK) return mlp ? pick_fmt<FMT_BLOCK, 1>(vi) : pick_fmt<FMT_BLOCK, 0>(vi);
+  return mlp ? pick_fmt<FMT_MX, 1>(vi) : pick_fmt<FMT_MX, 0>(vi);
 }
 
 constexpr int LDS_PER_WG = 163840;  // gfx950: 160 KB of LDS per workgroup
@@ -1211,11 +1230,11 @@ Occupancy g_occ;
 
 // The XL variants may use up to all LDS the static part leaves; the
 // occupancy is taken at that maximum, so it holds for any smaller use.
-int grid_size(int MT, int fmt, int XL, int* out) {
+int grid_size(int MT, int fmt, int XL, bool mlp, int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SGD_EHIP;
   const int fi = fmt == FMT_BLOCK ? 0 : 1;
-  const int vi = var_index(MT, XL);
+  const int vi = var_index(MT, XL, mlp);
   std::lock_guard<std::mutex> lock(g_occ.mu);
   if (g_occ.cus[dev] == 0) {
     int cus = 0;
@@ -1224,7 +1243,7 @@ int grid_size(int MT, int fmt, int XL, int* out) {
     g_occ.cus[dev] = cus;
   }
   if (g_occ.per_cu[dev][fi][vi] == 0) {
-    const void* kern = pick_kernel(MT, fmt, XL);
+    const void* kern = pick_kernel(MT, fmt, XL, mlp);
     const int dyn = XL ? LDS_PER_WG - (int)static_lds(MT) : 0;
     if (XL && hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess)
       return SGD_EHIP;
@@ -1252,7 +1271,7 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   const int MT = mt_for(pr.M);
   const int XL = use_xl(pr.fmt, MT, pr.K1) ? 1 : 0;
   int G = 0;
-  int rc = grid_size(MT, pr.fmt, XL, &G);
+  int rc = grid_size(MT, pr.fmt, XL, mlp, &G);
   if (rc != SGD_OK) return rc;
   if (G > MAX_WG) G = MAX_WG;
   const Plan p = make_plan(pr.fmt, pr.M, pr.K1, F, pr.w2->N, pr.w2->K, mlp, G);
@@ -1294,7 +1313,7 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.dn = p.dn;
   void* args[] = {&a};
   const size_t dyn = XL ? (size_t)((xl_bytes(pr.fmt, p.Mpad, pr.K1) + 15) & ~15) : 0;
-  return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt, XL), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, dyn, s));
+  return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt, XL, mlp), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, dyn, s));
 }
 
 }  // namespace sgd
