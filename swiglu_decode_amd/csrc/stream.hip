@@ -63,7 +63,22 @@ struct Cfg {
   // ready, measured slower: their traffic competes with the last gate/up
   // loads, which are on the critical path)
   static constexpr int PD = P;
+  // Gate/up with the activations staged in LDS (row tiles of 64 and 128
+  // rows, when every workgroup holds at most NS whole bands): each streaming
+  // wavefront owns one band over all of K with a PG-deep weight ring, and
+  // the sync wavefront stages Q(x) one k-tile at a time into DA LDS stages
+  // that all streaming wavefronts read.
+  static constexpr bool KS = MT >= 4;
+  static constexpr int PG = 8;
+  static constexpr int DA = MT >= 8 ? 3 : 4;
 };
+
+// One LDS stage of staged gate/up activations: per m-tile the 2 KB operand
+// tile in lane order (lane l's 32 bytes at l*16 and 1024 + l*16), then the
+// k-tile's row scales (block: fp32 per row; mx: the dword of a row's four
+// E8M0 bytes), 16*MT entries of 4 bytes.
+template <int MT>
+__host__ __device__ constexpr int ks_stage_bytes() { return MT * 2048 + MT * 64; }
 
 struct Phase {
   int KT;       // k-tiles of the weight's K
@@ -100,6 +115,7 @@ struct Args {
   int G;                     // workgroups in the grid
   int n_pairs, n_items;      // x quantization: (k-group, row tile) pairs, dealt into items
   int ngroups;               // F / 128
+  int ks;                    // gate/up with LDS-staged activations (Cfg::KS variants)
   Phase gu, dn;
 };
 
@@ -188,6 +204,8 @@ struct Lds {
   uint32_t consumed;               // band events the sync wavefront has taken
   uint32_t xq_ok;                  // Q(x) complete
   uint32_t rdy[MAX_GROUPS / 32];   // bit g: group g of Q(a) (k-tile g of the second GEMM) is ready
+  uint32_t a_ready;                // staged gate/up: k-tiles of Q(x) staged so far
+  uint32_t prog[NS];               // staged gate/up: k-tiles each streaming wavefront has used
 };
 
 __device__ __forceinline__ uint32_t lds_load(const uint32_t* p) {
@@ -231,6 +249,9 @@ struct Ring {
   v4f XB[P][MT];
   uint32_t X0[P][MT];
 };
+
+template <int MT, int FMT>
+__device__ void finish_gu_band(const Args& a, int b, v4f (&s)[2][MT]);
 
 template <int MT, int FMT, int P, int XL>
 struct Streamer {
@@ -288,8 +309,8 @@ struct Streamer {
   }
 
   // ---- loads of one ring slot (unconditional: fillers read past the end) ----
-  template <bool GU, int PP>
-  __device__ __forceinline__ void load_b(Ring<MT, PP>& R, int s, const ChunkPos& cp, int KT, int k) {
+  template <bool GU, class Rg>
+  __device__ __forceinline__ void load_b(Rg& R, int s, const ChunkPos& cp, int KT, int k) {
     const int kt_ = cp.kt0 + k;
     const bool ok = cp.ok && kt_ < KT;
     const uint32_t kt = ok ? (uint32_t)kt_ : 0u;
@@ -447,6 +468,101 @@ struct Streamer {
         }
       }
     }
+  }
+
+  // Staged gate/up: the weights of band `band` at k-tile kt (ring slot s)
+  // times every m-tile of the LDS stage, in the arithmetic of step_gu.
+  template <class Rg>
+  __device__ __forceinline__ void step_gu_staged(Rg& R, int s, int kt, const uint8_t* st, v4f (&acc)[2][MT]) {
+    const int l = lane_id();
+    const int sh = 8 * (kt & 3);
+    v8bf b[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float s0 = 1.0f, s1 = 1.0f;
+      if (FMT == FMT_MX) {
+        s0 = pow2_pos((int)((R.S0[s][nb] >> sh) & 0xFFu) - 127);
+        s1 = pow2_pos((int)((R.S1[s][nb] >> sh) & 0xFFu) - 127);
+      }
+      const v8i w = R.RB[s][nb];
+      b[nb][0] = widen8((uint32_t)w[0], (uint32_t)w[1], s0);
+      b[nb][1] = widen8((uint32_t)w[2], (uint32_t)w[3], s0);
+      b[nb][2] = widen8((uint32_t)w[4], (uint32_t)w[5], s1);
+      b[nb][3] = widen8((uint32_t)w[6], (uint32_t)w[7], s1);
+    }
+    const uint8_t* sc = st + MT * 2048;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const v8i x = make_v8i(*reinterpret_cast<const uint4*>(st + mt * 2048 + l * 16),
+                             *reinterpret_cast<const uint4*>(st + mt * 2048 + 1024 + l * 16));
+      float s0 = 1.0f, s1 = 1.0f;
+      v4f xb = {1.f, 1.f, 1.f, 1.f};
+      if (FMT == FMT_MX) {
+        const uint32_t e = reinterpret_cast<const uint32_t*>(sc)[mt * 16 + (l & 15)];
+        s0 = pow2_pos((int)((e >> xsh) & 0xFFu) - 127);
+        s1 = pow2_pos((int)((e >> (xsh + 16u)) & 0xFFu) - 127);
+      } else {
+        xb = *reinterpret_cast<const v4f*>(sc + (16 * mt + 4 * (l >> 4)) * 4);
+      }
+      v8bf av[4];
+      av[0] = widen8((uint32_t)x[0], (uint32_t)x[1], s0);
+      av[1] = widen8((uint32_t)x[2], (uint32_t)x[3], s0);
+      av[2] = widen8((uint32_t)x[4], (uint32_t)x[5], s1);
+      av[3] = widen8((uint32_t)x[6], (uint32_t)x[7], s1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if (FMT == FMT_BLOCK) {
+          v4f t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], b[nb][i], t, 0, 0, 0);
+          acc[nb][mt] += t * (xb * __uint_as_float(R.S0[s][nb]));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], b[nb][i], acc[nb][mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Staged gate/up for this wavefront's band (the q-th of the workgroup's
+  // whole bands, if it has one): all k-tiles in order, the activations from
+  // the LDS stages, then the band's SiLU, write-out and group accounting.
+  template <int NS, int NSLOT>
+  __device__ __forceinline__ void run_gu_staged(Lds<MT, NS, NSLOT>& L, const uint8_t* stages) {
+    constexpr int PG = Cfg<MT>::PG, DA = Cfg<MT>::DA, SB = ks_stage_bytes<MT>();
+    const Phase& ph = a.gu;
+    const int W = blockIdx.x;
+    if (W >= ph.nwg) return;
+    const int band = range_start(ph, W) / ph.CPB + q;
+    if (band >= range_start(ph, W + 1) / ph.CPB) return;
+    const int KT = ph.KT;
+    make_resources<PK_GU>();
+    struct {
+      v8i RB[PG][2];
+      uint32_t S0[PG][2], S1[PG][2];
+    } R;
+    const ChunkPos cp{1, band, 0};
+#pragma unroll
+    for (int s = 0; s < PG; ++s) load_b<true>(R, s, cp, KT, s);
+    v4f acc[2][MT];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < KT; k0 += PG) {
+#pragma unroll
+      for (int s = 0; s < PG; ++s) {
+        const int kt = k0 + s;
+        if (kt < KT) {
+          lds_wait_geq(&L.a_ready, (uint32_t)(kt + 1));
+          step_gu_staged(R, s, kt, stages + (kt % DA) * SB, acc);
+          if (lane_id() == 0) lds_store(&L.prog[q], (uint32_t)(kt + 1));
+        }
+        load_b<true>(R, s, cp, KT, kt + PG);  // past K: a filler
+      }
+    }
+    finish_gu_band<MT, FMT>(a, band, acc);
   }
 
   // Wait until the groups of Q(a) that chunk cp reads are ready (its k-tiles
@@ -918,7 +1034,7 @@ __device__ __forceinline__ void take_event(Lds<MT, NS, NSLOT>& L, int k, v4f (&s
 }
 
 template <int MT, int FMT>
-__device__ __forceinline__ void finish_gu_band(const Args& a, int b, v4f (&s)[2][MT]) {
+__device__ void finish_gu_band(const Args& a, int b, v4f (&s)[2][MT]) {
   const int l = lane_id();
   const Phase& ph = a.gu;
   const int nsh = owner_wg(ph, b * ph.CPB + ph.CPB - 1) - owner_wg(ph, b * ph.CPB) + 1;
@@ -966,8 +1082,77 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
       }
 }
 
+// Staged gate/up: copy Q(x) (workspace, m-tile order) into the LDS stages
+// one k-tile at a time, for the nst streaming wavefronts that hold a band.
+// Stage kt % DA is rewritten once every one of them has used k-tile kt - DA;
+// LD k-tiles are in flight in registers.
+template <int MT, int FMT, int NS, int NSLOT>
+__device__ __forceinline__ void stage_activations(const Args& a, Lds<MT, NS, NSLOT>& L, uint8_t* stages, int nst) {
+  constexpr int DA = Cfg<MT>::DA, SB = ks_stage_bytes<MT>(), LD = 2;
+  const int l = lane_id();
+  const uint32_t r = (uint32_t)(l & 15), g = (uint32_t)(l >> 4);
+  const int KT = a.gu.KT;
+  const uint32_t KT1 = (uint32_t)(a.K1 >> 7);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xa, (uint32_t)a.M * (uint32_t)a.K1);
+  const __amdgpu_buffer_rsrc_t rxs =
+      make_rsrc(a.xs, FMT == FMT_BLOCK ? KT1 * (uint32_t)a.Mpad * 4u : (uint32_t)a.M * (KT1 * 4u));
+  uint4 cb[LD][MT][2];
+  uint32_t sb[LD][2];
+  auto issue = [&](int u, int kt) {
+    const bool okk = kt < KT;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int Mt = min(16, a.M - 16 * mt);
+      const bool v = okk && (int)r < Mt;
+      const uint32_t uMt = (uint32_t)max(Mt, 0);
+      const uint32_t o = (uint32_t)mt * 16u * (uint32_t)a.K1 + ((uint32_t)kt * 8u + g) * 16u * uMt + r * 16u;
+      cb[u][mt][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, v ? o : OOB, 0, 0));
+      cb[u][mt][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, v ? o + 64u * uMt : OOB, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = 2 * l + j;  // row e % 16 of m-tile e / 16 (16*MT entries: lanes < 8*MT)
+      uint32_t off = OOB;
+      if (e >= 16 * MT) {
+      } else if (FMT == FMT_BLOCK) {
+        if (okk) off = ((uint32_t)kt * (uint32_t)a.Mpad + (uint32_t)e) * 4u;
+      } else {
+        const int mt = e >> 4, rr = e & 15;
+        const int Mt = min(16, a.M - 16 * mt);
+        if (okk && rr < Mt)
+          off = (uint32_t)mt * 16u * KT1 * 4u + (uint32_t)kt * 4u * (uint32_t)Mt + (uint32_t)rr * 4u;
+      }
+      sb[u][j] = ld_coherent_u32(rxs, off);
+    }
+  };
+  auto write = [&](int u, int kt) {
+    uint8_t* st = stages + (kt % DA) * SB;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      *reinterpret_cast<uint4*>(st + mt * 2048 + l * 16) = cb[u][mt][0];
+      *reinterpret_cast<uint4*>(st + mt * 2048 + 1024 + l * 16) = cb[u][mt][1];
+    }
+    if (l < 8 * MT) *reinterpret_cast<uint2*>(st + MT * 2048 + l * 8) = make_uint2(sb[u][0], sb[u][1]);
+  };
+#pragma unroll
+  for (int u = 0; u < LD; ++u) issue(u, u);
+  for (int k0 = 0; k0 < KT; k0 += LD) {
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const int kt = k0 + u;
+      if (kt < KT) {
+        if (kt >= DA)
+          for (int w = 0; w < nst; ++w) lds_wait_geq(&L.prog[w], (uint32_t)(kt - DA + 1));
+        write(u, kt);
+        if (l == 0) lds_store(&L.a_ready, (uint32_t)(kt + 1));
+      }
+      issue(u, kt + LD);
+    }
+  }
+}
+
 template <int MT, int FMT, int XL, int NS, int NSLOT>
-__device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L) {
+__device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, uint8_t* stages) {
   const int l = lane_id();
   const int W = blockIdx.x;
   const int rep = W & (NREP - 1);
@@ -987,7 +1172,11 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L) 
   if (a.mlp && W < a.gu.nwg) {
     const Phase& ph = a.gu;
     const int c0 = range_start(ph, W), c1 = range_start(ph, W + 1);
-    if (c0 < c1) {
+    if (Cfg<MT>::KS && a.ks) {
+      // the streaming wavefronts finish their own bands
+      const int nst = min((c1 - c0) / ph.CPB, NS);
+      if (nst > 0) stage_activations<MT, FMT>(a, L, stages, nst);
+    } else if (c0 < c1) {
       for (int b = c0 / ph.CPB; b <= (c1 - 1) / ph.CPB; ++b) {
         v4f s[2][MT];
         take_event(L, k++, s);
@@ -1051,6 +1240,8 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     L.consumed = 0u;
     L.xq_ok = XL ? 1u : 0u;
     for (int i = 0; i < MAX_GROUPS / 32; ++i) L.rdy[i] = 0u;
+    L.a_ready = 0u;
+    for (int i = 0; i < C::NS; ++i) L.prog[i] = 0u;
   }
   __syncthreads();
   if (wv == 0) {
@@ -1060,7 +1251,7 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
       xq.finish(a, lds_x, 16 * MT);
       __syncthreads();
     }
-    sync_wave<MT, FMT, XL>(a, L);
+    sync_wave<MT, FMT, XL>(a, L, lds_x);
   } else {
     Streamer<MT, FMT, C::P, XL> st(a, wv - 1, lds_x);
     int k = 0;
@@ -1080,7 +1271,10 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     };
     auto nothing = []() {};
     if (MLP) {
-      st.template run_phase<PK_GU, C::P>(L, k, quantize_x);
+      if (C::KS && a.ks)
+        st.run_gu_staged(L, lds_x);
+      else
+        st.template run_phase<PK_GU, C::P>(L, k, quantize_x);
       st.template run_phase<PK_DN, C::PD>(L, k, nothing);
     } else {
       st.template run_phase<PK_GEMM, C::P>(L, k, quantize_x);
@@ -1095,6 +1289,7 @@ namespace {
 
 struct Plan {
   int ok;
+  int ks;  // staged gate/up
   int MT, Mpad, G, n_pairs, n_items, ngroups;
   Phase gu, dn;
   size_t off_xa, off_xs, off_a32, off_aq, off_as, off_gpart, off_dpart, bytes;
@@ -1154,6 +1349,14 @@ Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp, int G) {
   // two bands (then most bands would be shared, and each shared band costs
   // a round trip through memory at its end)
   if (mlp) p.gu = make_phase(KT1, F / 16, P, NS, G, F / 16 < 2 * G);
+  // staged gate/up: whole bands over every workgroup, at most NS each
+  const int nb = F / 16, wks = nb < G ? nb : G;
+  p.ks = 0;
+  if (mlp && p.MT >= 4 && (nb + wks - 1) / wks <= NS) {
+    p.gu = make_phase(KT1, nb, P, NS, G, true);
+    p.gu.nwg = wks;
+    p.ks = 1;
+  }
   p.dn = make_phase(K2 / 128, N / 32, mlp ? cfg_pd(p.MT) : P, NS, G, false);
   p.ok = p.ngroups <= MAX_GROUPS && (!mlp || F / 16 <= MAX_GBANDS) && N / 32 <= CTRL_WORDS - C_DPCNT;
   size_t o = CTRL_BYTES;
@@ -1212,6 +1415,11 @@ size_t static_lds(int MT) {
     default: return sizeof(Lds<8, Cfg<8>::NS, Cfg<8>::NSLOT>);
   }
 }
+// LDS stages of the staged gate/up (the MLP variants with Cfg::KS).
+int ks_dyn(int MT, bool mlp) {
+  if (!mlp) return 0;
+  return MT == 4 ? Cfg<4>::DA * ks_stage_bytes<4>() : MT == 8 ? Cfg<8>::DA * ks_stage_bytes<8>() : 0;
+}
 // Q(x) goes to LDS when it fits beside the partial-sum slots (with margin).
 bool use_xl(int fmt, int MT, int K1) {
   if (MT > 2) return false;
@@ -1244,8 +1452,8 @@ int grid_size(int MT, int fmt, int XL, bool mlp, int* out) {
   }
   if (g_occ.per_cu[dev][fi][vi] == 0) {
     const void* kern = pick_kernel(MT, fmt, XL, mlp);
-    const int dyn = XL ? LDS_PER_WG - (int)static_lds(MT) : 0;
-    if (XL && hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess)
+    const int dyn = XL ? LDS_PER_WG - (int)static_lds(MT) : ks_dyn(MT, mlp);
+    if (dyn > 0 && hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess)
       return SGD_EHIP;
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 64 * cfg_nwave(MT), (size_t)dyn) != hipSuccess ||
@@ -1309,10 +1517,11 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.n_pairs = p.n_pairs;
   a.n_items = XL ? 0 : p.n_items;
   a.ngroups = p.ngroups;
+  a.ks = p.ks;
   a.gu = p.gu;
   a.dn = p.dn;
   void* args[] = {&a};
-  const size_t dyn = XL ? (size_t)((xl_bytes(pr.fmt, p.Mpad, pr.K1) + 15) & ~15) : 0;
+  const size_t dyn = XL ? (size_t)((xl_bytes(pr.fmt, p.Mpad, pr.K1) + 15) & ~15) : (size_t)ks_dyn(p.MT, mlp);
   return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt, XL, mlp), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, dyn, s));
 }
 
