@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--ffn", type=int, default=12288)
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain streaming-read measurement (profiling runs of the fused kernel)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="instead of the benchmark, run a plain elementwise copy of this many bytes "
                          "(read once, written once) three times: the reference for HBM byte counters")
@@ -197,7 +199,7 @@ def main():
                 algorithmic_bytes_per_launch=per_m[rm]["bytes"],
                 traffic_bytes_per_launch=int(tb) if tb else None)
 
-    ceiling = read_ceiling(dev)
+    ceiling = None if args.no_read_ceiling else read_ceiling(dev)
 
     cpu = None
     parity = None
