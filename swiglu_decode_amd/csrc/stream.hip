@@ -421,6 +421,7 @@ struct Streamer {
       av[mt][2] = widen8((uint32_t)x[4], (uint32_t)x[5], s1);
       av[mt][3] = widen8((uint32_t)x[6], (uint32_t)x[7], s1);
     }
+    v8bf b[2][4];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       float s0 = 1.0f, s1 = 1.0f;
@@ -429,24 +430,37 @@ struct Streamer {
         s1 = pow2_pos((int)((R.S1[s][nb] >> sh) & 0xFFu) - 127);
       }
       const v8i w = R.RB[s][nb];
-      v8bf b[4];
-      b[0] = widen8((uint32_t)w[0], (uint32_t)w[1], s0);
-      b[1] = widen8((uint32_t)w[2], (uint32_t)w[3], s0);
-      b[2] = widen8((uint32_t)w[4], (uint32_t)w[5], s1);
-      b[3] = widen8((uint32_t)w[6], (uint32_t)w[7], s1);
+      b[nb][0] = widen8((uint32_t)w[0], (uint32_t)w[1], s0);
+      b[nb][1] = widen8((uint32_t)w[2], (uint32_t)w[3], s0);
+      b[nb][2] = widen8((uint32_t)w[4], (uint32_t)w[5], s1);
+      b[nb][3] = widen8((uint32_t)w[6], (uint32_t)w[7], s1);
+    }
+    // 32-deep steps outermost: consecutive matrix instructions feed
+    // independent accumulators (each accumulator's own order is unchanged)
+    if (FMT == FMT_BLOCK) {
+      v4f t[2][MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (FMT == FMT_BLOCK) {
-          v4f t = {0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[i], t, 0, 0, 0);
-          acc[nb][mt] += t * (R.XB[sa][mt] * __uint_as_float(R.S0[s][nb]));
-        } else {
+        for (int mt = 0; mt < MT; ++mt) t[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[i], acc[nb][mt], 0, 0, 0);
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) t[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[nb][i], t[nb][mt], 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[nb][mt] += t[nb][mt] * (R.XB[sa][mt] * __uint_as_float(R.S0[s][nb]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[nb][i], acc[nb][mt], 0, 0, 0);
     }
   }
 
@@ -491,37 +505,51 @@ struct Streamer {
       b[nb][3] = widen8((uint32_t)w[6], (uint32_t)w[7], s1);
     }
     const uint8_t* sc = st + MT * 2048;
+    v8bf av[MT][4];
+    v4f xb[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const v8i x = make_v8i(*reinterpret_cast<const uint4*>(st + mt * 2048 + l * 16),
                              *reinterpret_cast<const uint4*>(st + mt * 2048 + 1024 + l * 16));
       float s0 = 1.0f, s1 = 1.0f;
-      v4f xb = {1.f, 1.f, 1.f, 1.f};
+      xb[mt] = v4f{1.f, 1.f, 1.f, 1.f};
       if (FMT == FMT_MX) {
         const uint32_t e = reinterpret_cast<const uint32_t*>(sc)[mt * 16 + (l & 15)];
         s0 = pow2_pos((int)((e >> xsh) & 0xFFu) - 127);
         s1 = pow2_pos((int)((e >> (xsh + 16u)) & 0xFFu) - 127);
       } else {
-        xb = *reinterpret_cast<const v4f*>(sc + (16 * mt + 4 * (l >> 4)) * 4);
+        xb[mt] = *reinterpret_cast<const v4f*>(sc + (16 * mt + 4 * (l >> 4)) * 4);
       }
-      v8bf av[4];
-      av[0] = widen8((uint32_t)x[0], (uint32_t)x[1], s0);
-      av[1] = widen8((uint32_t)x[2], (uint32_t)x[3], s0);
-      av[2] = widen8((uint32_t)x[4], (uint32_t)x[5], s1);
-      av[3] = widen8((uint32_t)x[6], (uint32_t)x[7], s1);
+      av[mt][0] = widen8((uint32_t)x[0], (uint32_t)x[1], s0);
+      av[mt][1] = widen8((uint32_t)x[2], (uint32_t)x[3], s0);
+      av[mt][2] = widen8((uint32_t)x[4], (uint32_t)x[5], s1);
+      av[mt][3] = widen8((uint32_t)x[6], (uint32_t)x[7], s1);
+    }
+    // (matrix instructions ordered as in step_gu)
+    if (FMT == FMT_BLOCK) {
+      v4f t[2][MT];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (FMT == FMT_BLOCK) {
-          v4f t = {0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], b[nb][i], t, 0, 0, 0);
-          acc[nb][mt] += t * (xb * __uint_as_float(R.S0[s][nb]));
-        } else {
+        for (int mt = 0; mt < MT; ++mt) t[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], b[nb][i], acc[nb][mt], 0, 0, 0);
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) t[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[nb][i], t[nb][mt], 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[nb][mt] += t[nb][mt] * (xb[mt] * __uint_as_float(R.S0[s][nb]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][i], b[nb][i], acc[nb][mt], 0, 0, 0);
     }
   }
 
