@@ -572,7 +572,12 @@ struct Streamer {
     } R;
     const ChunkPos cp{1, band, 0};
 #pragma unroll
-    for (int s = 0; s < PG; ++s) load_b<true>(R, s, cp, KT, s);
+    for (int s = 0; s < 2; ++s) load_b<true>(R, s, cp, KT, s);
+    // the rest once Q(x) exists: a full prefetch at launch would delay the
+    // x quantization and its cross-workgroup flags (measured)
+    lds_wait_geq(&L.xq_ok, 1u);
+#pragma unroll
+    for (int s = 2; s < PG; ++s) load_b<true>(R, s, cp, KT, s);
     v4f acc[2][MT];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)

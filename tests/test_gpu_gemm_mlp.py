@@ -31,7 +31,7 @@ def test_scaled_gemm_parity(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["block", "mx"])
-@pytest.mark.parametrize("M", [1, 5, 16, 33, 64, 128])
+@pytest.mark.parametrize("M", [1, 5, 16, 33, 48, 64, 100, 128])
 @pytest.mark.parametrize("d_,F", [(256, 768), (512, 1536), (640, 1152)])
 def test_fused_mlp_parity(fmt, M, d_, F):
     d = dev()
