@@ -143,8 +143,10 @@ int sgd_quantize_act(int fmt, const uint16_t* x_bf16, int M, int K,
  * activations, the SwiGLU intermediate, split-K partial sums and
  * synchronisation counters.  Its first 256 KB are a control block that must
  * be zero-filled ONCE after allocation (sgd_workspace_clear or any fill
- * kernel); every call leaves it zero again on exit, so one workspace can
- * serve calls of any shape that fit in it.  Calls that share a workspace
+ * kernel); every call that completes leaves it ready for the next (counters
+ * zero, flags holding the number of the launch that raised them), so one
+ * workspace can serve calls of any shape that fit in it.  After a call that
+ * did not complete (a device fault), clear it again.  Calls that share a workspace
  * must not overlap (serialise them on one stream).  Size in bytes; 0 on
  * invalid arguments or when the shape needs more counters than the control
  * block holds (the output width N, or d of the MLP, must be <= 860160).

@@ -134,7 +134,8 @@ def mlp_workspace_bytes(fmt, M, d, ffn):
 
 class Workspace:
     """A zero-initialised device workspace that grows on demand.  The kernels
-    leave its control block zeroed after every call; calls sharing one
+    leave its control block ready for the next call (counters zero, flags
+    holding the number of the launch that raised them); calls sharing one
     workspace must be serialised on one stream."""
 
     def __init__(self, device, nbytes=0):

@@ -202,6 +202,8 @@ __device__ __forceinline__ void wait_geq(const uint32_t* p, uint32_t target) {
 // Buffer resource over [base, base + bytes); loads through it with the sc1
 // cache policy are agent-coherent, and offsets past `bytes` read as zero.
 constexpr int AUX_SC1 = 16;
+// Cache-policy bit of a non-temporal (streaming) access.
+constexpr int AUX_NT = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

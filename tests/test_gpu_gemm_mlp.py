@@ -48,7 +48,7 @@ def test_fused_mlp_parity(fmt, M, d_, F):
 
 @pytest.mark.parametrize("fmt", ["block", "mx"])
 def test_repeated_calls_and_shrinking_m_share_a_workspace(fmt):
-    # the control block must be left zeroed: back-to-back calls, then a smaller M
+    # the control block must be left ready: back-to-back calls, then a smaller M
     d = dev()
     note(f"repeat {fmt}")
     wl = synth.Workload("t", 512, 1536, (64,), (fmt,), 3001)
@@ -121,3 +121,34 @@ def test_permuted_scales_are_caught(fmt):
     err = ref.rel_fro(gpu_out_f64(bad), yr)
     print(f"[parity] permuted scales rel_fro={err:.3f}")
     assert err > 0.1
+
+
+# Word of the control block that counts completed launches (flags are raised
+# with the current launch's number, so they need no clearing between calls).
+LAUNCH_COUNT_WORD = 64
+
+
+@pytest.mark.parametrize("fmt,M", [("mx", 4), ("block", 64)])
+def test_launch_number_wrap(fmt, M):
+    # preset the launch count just below 2**32 - 1: the calls then use launch
+    # numbers 0xFFFFFFFE, 0xFFFFFFFF (which clears every flag on exit), 1, 2;
+    # each must equal the first call on a fresh workspace, bit for bit
+    d = dev()
+    note(f"launch-number wrap {fmt} M={M}")
+    wl = synth.Workload("t", 1024, 3072, (M,), (fmt,), 3004)
+    inp = synth.mlp_inputs(wl, M)
+    pws = [sgd.quantize_pack_weight(inp[k].to(d), fmt) for k in ("wg", "wu", "wd")]
+    x = inp["x"].to(d)
+    ws0 = sgd.Workspace(d, sgd.mlp_workspace_bytes(fmt, M, 1024, 3072))
+    y0 = sgd.fused_swiglu_mlp(x, *pws, workspace=ws0).clone()
+    ws = sgd.Workspace(d, sgd.mlp_workspace_bytes(fmt, M, 1024, 3072))
+    ws.tensor[4 * LAUNCH_COUNT_WORD:4 * LAUNCH_COUNT_WORD + 4].copy_(
+        torch.tensor([0xFD, 0xFF, 0xFF, 0xFF], dtype=torch.uint8))
+    ys = [sgd.fused_swiglu_mlp(x, *pws, workspace=ws).clone() for _ in range(4)]
+    torch.cuda.synchronize()
+    count = int(ws.tensor[4 * LAUNCH_COUNT_WORD:4 * LAUNCH_COUNT_WORD + 4].cpu().view(torch.int32)[0])
+    assert count == 2, count
+    for i, y in enumerate(ys):
+        assert torch.equal(y, y0), f"call {i} after the preset differs"
+    q = [oracle_weight(inp[k], fmt) for k in ("wg", "wu", "wd")]
+    assert_close(gpu_out_f64(y0), ref.swiglu_mlp(bf16_to_f64(inp["x"]), *q), f"wrap {fmt} M={M}")
