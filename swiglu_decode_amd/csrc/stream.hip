@@ -1118,92 +1118,15 @@ __device__ void finish_gu_band(const Args& a, int b, v4f (&s)[2][MT], uint32_t e
   raise_flag(a.ctrl, PG_RDY, grp, ep);
 }
 
-// Split-K combine of a second-GEMM band shared by workgroups w0..w1: every
-// workgroup but w1 (whose k-range reads the latest groups of Q(a), so it
-// usually ends last) stores its partial sums and arrives; w1 waits for those
-// arrivals and adds the stored sums in workgroup order, then its own.  (The
-// same order as a sum over all stored partials; one round trip less for the
-// workgroup that ends last.)  True in w1.
-template <int MT>
-__device__ __forceinline__ bool combine_dn(const Args& a, int b, v4f (&s)[2][MT]) {
-  const int l = lane_id();
-  const Phase& ph = a.dn;
-  const int w0 = owner_wg(ph, b * ph.CPB), w1 = owner_wg(ph, b * ph.CPB + ph.CPB - 1);
-  if (w0 == w1) return true;
-  uint32_t* cnt = a.ctrl + C_DPCNT + b;
-  const int W = blockIdx.x;
-  const int side = band_side(ph, W, b);
-  if (W != w1) {
-    if (MT <= 2) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int row = mt * 16 + 4 * (l >> 4) + rr;
-            if (row < a.M)
-              st_coherent(a.dpart + ((((size_t)W * 2 + side) * 2 + nb) * a.M + row) * 16 + (l & 15), s[nb][mt][rr]);
-          }
-    } else {
-      const __amdgpu_buffer_rsrc_t r = part_rsrc<MT>(a, a.dpart);
-      const uint32_t base = ((uint32_t)W * 2u + (uint32_t)side) * part_slot_bytes<MT>();
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          st_coherent_b128(r, base + (uint32_t)(((nb * MT + mt) * 64 + l) * 16), __builtin_bit_cast(uint4, s[nb][mt]));
-    }
-    drain_memory();
-    if (l == 0) atomic_add_agent(cnt, 1u);
-    return false;
-  }
-  wait_geq(cnt, (uint32_t)(w1 - w0));
-  if (l == 0) store_agent(cnt, 0u);  // (its last use in this launch)
-  v4f t[2][MT];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) t[nb][mt] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (MT <= 2) {
-    for (int w = w0; w < w1; ++w) {
-      const float* base = a.dpart + ((size_t)w * 2 + band_side(ph, w, b)) * 2 * a.M * 16;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int row = min(mt * 16 + 4 * (l >> 4) + rr, a.M - 1);
-            t[nb][mt][rr] += ld_coherent(base + ((size_t)nb * a.M + row) * 16 + (l & 15));
-          }
-    }
-  } else {
-    const __amdgpu_buffer_rsrc_t r = part_rsrc<MT>(a, a.dpart);
-    for (int w = w0; w < w1; ++w) {
-      const uint32_t base = ((uint32_t)w * 2u + (uint32_t)band_side(ph, w, b)) * part_slot_bytes<MT>();
-      v4f u[2][MT];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) u[nb][mt] = ld_coherent_v4f(r, base + (uint32_t)(((nb * MT + mt) * 64 + l) * 16));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) t[nb][mt] += u[nb][mt];
-    }
-  }
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s[nb][mt] = t[nb][mt] + s[nb][mt];
-  return true;
-}
-
 template <int MT>
 __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2][MT]) {
   const int l = lane_id();
-  if (!combine_dn<MT>(a, b, s)) return;
+  const Phase& ph = a.dn;
+  const int nsh = owner_wg(ph, b * ph.CPB + ph.CPB - 1) - owner_wg(ph, b * ph.CPB) + 1;
+  if (nsh > 1) {
+    if (!arrive_shared<MT>(a, ph, a.dpart, a.ctrl + C_DPCNT, b, s, nsh)) return;
+    sum_shared<MT>(a, ph, a.dpart, b, s);
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
