@@ -1,6 +1,7 @@
 """The fused MLP and the scaled GEMM captured in a HIP graph: several replays,
 with eager work and synchronisations between them, each equal to the eager
-result bit for bit (the kernels leave the workspace's control block zeroed
+result bit for bit (the kernels leave the workspace's control block ready
+for the next launch, with counters zero and flags holding the launch number,
 and record no memset)."""
 
 import pytest
