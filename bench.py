@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the plain streaming-read measurement (profiling runs of the fused kernel)")
+    ap.add_argument("--stack", action="store_true",
+                    help="instead of the single-MLP benchmark, time the whole decode step of the 24-block "
+                         "stack (d=2560, ffn=9728, 128x128 block fp8, M=64, bf16 head 4096x2560) as one hipGraph")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="instead of the benchmark, run a plain elementwise copy of this many bytes "
                          "(read once, written once) three times: the reference for HBM byte counters")
@@ -128,6 +131,10 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 3}))
+        return
+
+    if args.stack:
+        bench_stack(args, dev)
         return
 
     import swiglu_decode_amd as sgd
@@ -228,6 +235,94 @@ def main():
         "read_stream_ceiling": ceiling,
         "cpu_baseline": cpu,
         "parity": parity,
+    }
+    print(json.dumps(out))
+
+
+def bench_stack(args, dev):
+    """The decode step of the 24-block stack: h = f32(x); per block
+    x_l = bf16(RMSNorm(h)), y_l = fused MLP(x_l), h += y_l (the add and the
+    next block's RMSNorm in one launch); then the bf16 head
+    and the argmax of every row.  All 24 packed layers stay resident (1.8 GB,
+    far beyond the Infinity Cache, so each step reads them cold); the step is
+    captured once as a hipGraph and replayed, timed with HIP events on its
+    stream.  Algorithmic bytes per step = per block (fp8 weights + scales +
+    bf16 x_l + bf16 y_l) + bf16 head + f32 logits."""
+    import torch
+    import swiglu_decode_amd as sgd
+    import synth
+    wl = synth.WORKLOADS["stack"]
+    M, d, F = wl.ms[0], wl.d, wl.ffn
+    layers = []
+    for layer in range(wl.layers):
+        layers.append([sgd.quantize_pack_weight(w.to(dev), "block") for w in synth.stack_layer_weights(wl, layer)])
+    head = synth.stack_head(wl).to(dev)
+    x = synth.stack_x(wl, M).to(dev)
+    h = torch.empty((M, d), dtype=torch.float32, device=dev)
+    xb = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    lg = torch.empty((M, wl.vocab), dtype=torch.float32, device=dev)
+    tok = torch.empty((M,), dtype=torch.int32, device=dev)
+    ws = sgd.Workspace(dev, sgd.mlp_workspace_bytes("block", M, d, F))
+    layer_bytes = sum(int(p.codes.numel()) + int(p.scales.numel()) for p in layers[0]) + 2 * M * d * 2
+    step_bytes = wl.layers * layer_bytes + int(head.numel()) * 2 + M * wl.vocab * 4
+
+    def step():
+        # (the residual add of a block and the RMSNorm of the next in one launch)
+        sgd.bf16_to_f32(x, out=h)
+        sgd.rmsnorm_bf16(h, out=xb)
+        for i, pws in enumerate(layers):
+            sgd.fused_swiglu_mlp(xb, *pws, out=y, workspace=ws)
+            if i + 1 < len(layers):
+                sgd.residual_rmsnorm_bf16(h, y, out=xb)
+            else:
+                sgd.residual_add(h, y)
+        sgd.head_logits(h, head, out=lg)
+        sgd.argmax_rows(lg, out=tok)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step()
+        stream.synchronize()
+        tok_eager = tok.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        stream.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        t1.record(stream)
+        t1.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    same = bool(torch.equal(tok, tok_eager))
+    gbs = step_bytes / us / 1e3
+    out = {
+        "metric": "decode step of the 24-block fp8 SwiGLU stack: us/step and algorithmic HBM GB/s",
+        "value": round(us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.layers} x (RMSNorm, fused SwiGLU MLP d={d} ffn={F} 128x128 block fp8, "
+                               f"residual add) + bf16 head {wl.vocab}x{d} + argmax, M={M}, one hipGraph",
+                   "layers": wl.layers, "d": d, "ffn": F, "M": M, "vocab": wl.vocab, "fmt": "block",
+                   "parallelism": "single GPU"},
+        "us_per_block": round(us / wl.layers, 2),
+        "algorithmic_bytes_per_step": step_bytes,
+        "gbs": round(gbs, 1),
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "graph_tokens_equal_eager": same,
     }
     print(json.dumps(out))
 

@@ -203,6 +203,15 @@ int sgd_rmsnorm_bf16(const float* h, int M, int d, float eps, uint16_t* x_bf16,
 /* h [M, d] fp32 += y [M, d] bf16 (the residual add). */
 int sgd_residual_add(float* h, const uint16_t* y_bf16, int M, int d, void* stream);
 
+/* The residual add and the next block's RMSNorm in one launch: h += y, then
+ * x = bf16( h / sqrt(mean(h^2) + eps) ) per row, unit gain.  Bit-identical
+ * to sgd_residual_add followed by sgd_rmsnorm_bf16 (one pass less over h and
+ * one launch less between two blocks).  h [M, d] fp32 is updated in place;
+ * y, x [M, d] bf16; all 16-byte aligned; d multiple of 128.  x must not
+ * overlap h or y. */
+int sgd_residual_rmsnorm_bf16(float* h, const uint16_t* y_bf16, int M, int d, float eps,
+                              uint16_t* x_bf16, void* stream);
+
 /* logits [M, N] fp32 = bf16(h) [M, K] * W^T with W [N, K] bf16 row-major,
  * fp32 accumulation (the bf16 output head).  h is fp32 and is rounded to
  * bf16 (nearest-even) on load.  M <= 128, N and K multiples of 128. */

@@ -237,6 +237,20 @@ def residual_add(h, y):
     return h
 
 
+def residual_rmsnorm_bf16(h, y, eps=1e-6, out=None):
+    """h += y, then the next block's input x = bf16(RMSNorm(h)), in one
+    launch (bit-identical to residual_add followed by rmsnorm_bf16)."""
+    _need(h, "h", torch.float32)
+    M, d = h.shape
+    _need(y, "y", torch.bfloat16, (M, d), h.device)
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=h.device)
+    _need(out, "out", torch.bfloat16, (M, d), h.device)
+    _lib.check("sgd_residual_rmsnorm_bf16",
+               lib().sgd_residual_rmsnorm_bf16(_ptr(h), _ptr(y), M, d, float(eps), _ptr(out), _stream(h)))
+    return out
+
+
 def head_logits(h, w, out=None):
     _need(h, "h", torch.float32)
     M, K = h.shape

@@ -50,6 +50,7 @@ SIGNATURES = {
     "sgd_bf16_to_f32": (_i, [_vp, _i, _i, _vp, _vp]),
     "sgd_rmsnorm_bf16": (_i, [_vp, _i, _i, _f, _vp, _vp]),
     "sgd_residual_add": (_i, [_vp, _vp, _i, _i, _vp]),
+    "sgd_residual_rmsnorm_bf16": (_i, [_vp, _vp, _i, _i, _f, _vp, _vp]),
     "sgd_head_logits": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
     "sgd_argmax_rows": (_i, [_vp, _i, _i, _vp, _vp]),
     "sgd_read_stream": (_i, [_vp, _sz, _vp, _vp]),

@@ -189,6 +189,15 @@ int sgd_residual_add(float* h, const uint16_t* y_bf16, int M, int d, void* strea
   return launch_residual_add(h, y_bf16, M, d, as_stream(stream));
 }
 
+int sgd_residual_rmsnorm_bf16(float* h, const uint16_t* y_bf16, int M, int d, float eps, uint16_t* x_bf16,
+                              void* stream) {
+  if (!h || !y_bf16 || !x_bf16 || M <= 0 || d <= 0 || M > 65536 || d > MAX_DIM || !(eps >= 0.0f))
+    return SGD_EINVAL;
+  if (d % 128) return SGD_EDIM;
+  if (!al16(h) || !al16(y_bf16) || !al16(x_bf16)) return SGD_EALIGN;
+  return launch_residual_rmsnorm(h, y_bf16, M, d, eps, x_bf16, as_stream(stream));
+}
+
 int sgd_head_logits(const float* h, int M, int K, const uint16_t* w_bf16, int N, float* logits,
                     void* stream) {
   if (!h || !w_bf16 || !logits || M <= 0 || M > SGD_MAX_M) return SGD_EINVAL;

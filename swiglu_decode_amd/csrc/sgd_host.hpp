@@ -38,6 +38,7 @@ int launch_stream(const Problem& p, hipStream_t s);
 int launch_bf16_to_f32(const uint16_t* x, int M, int d, float* h, hipStream_t s);
 int launch_rmsnorm(const float* h, int M, int d, float eps, uint16_t* x, hipStream_t s);
 int launch_residual_add(float* h, const uint16_t* y, int M, int d, hipStream_t s);
+int launch_residual_rmsnorm(float* h, const uint16_t* y, int M, int d, float eps, uint16_t* x, hipStream_t s);
 int launch_head(const float* h, int M, int K, const uint16_t* w, int N, float* out, hipStream_t s);
 int launch_argmax(const float* logits, int M, int N, int32_t* out, hipStream_t s);
 

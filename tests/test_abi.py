@@ -106,6 +106,10 @@ def test_argument_errors_launch_nothing(L):
     # glue
     assert L.sgd_rmsnorm_bf16(P(0x1000), 4, 100, ctypes.c_float(1e-6), P(0x1000), None) == E["EDIM"]
     assert L.sgd_rmsnorm_bf16(P(0x1000), 4, 128, ctypes.c_float(-1.0), P(0x1000), None) == E["EINVAL"]
+    assert L.sgd_residual_rmsnorm_bf16(P(0x1000), P(0x2000), 4, 100, ctypes.c_float(1e-6), P(0x3000), None) == E["EDIM"]
+    assert L.sgd_residual_rmsnorm_bf16(P(0x1000), P(0x2000), 4, 128, ctypes.c_float(-1.0), P(0x3000), None) == E["EINVAL"]
+    assert L.sgd_residual_rmsnorm_bf16(None, P(0x2000), 4, 128, ctypes.c_float(1e-6), P(0x3000), None) == E["EINVAL"]
+    assert L.sgd_residual_rmsnorm_bf16(P(0x1000), P(0x2008), 4, 128, ctypes.c_float(1e-6), P(0x3000), None) == E["EALIGN"]
     assert L.sgd_head_logits(P(0x1000), 200, 256, P(0x1000), 256, P(0x1000), None) == E["EINVAL"]
     assert L.sgd_argmax_rows(P(0x1000), 0, 10, P(0x1000), None) == E["EINVAL"]
     assert L.sgd_workspace_clear(P(0x1000), 24, None) == E["EALIGN"]

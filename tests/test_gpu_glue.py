@@ -40,6 +40,28 @@ def test_rmsnorm_and_residual(M, dd):
     assert np.array_equal(f.cpu().numpy().astype(np.float64), bf16_to_f64(y))
 
 
+@pytest.mark.parametrize("M,dd", [(1, 128), (5, 384), (64, 2560), (3, 8192)])
+def test_residual_rmsnorm_equals_the_two_calls(M, dd):
+    # one launch for h += y and the next block's RMSNorm: bit-identical to
+    # residual_add followed by rmsnorm_bf16 (h and x)
+    d = dev()
+    note(f"residual+rmsnorm M={M} d={dd}")
+    rng = np.random.default_rng(17 + M)
+    h = torch.from_numpy((rng.standard_normal((M, dd)) * 3.0).astype(np.float32)).to(d)
+    y = synth.random_bf16((M, dd), 19 + M, 1.0).to(d)
+    h2 = h.clone()
+    sgd.residual_add(h, y)
+    x = sgd.rmsnorm_bf16(h, 1e-6)
+    x2 = sgd.residual_rmsnorm_bf16(h2, y, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(h2, h)
+    assert torch.equal(bf16_bits_t(x2), bf16_bits_t(x))
+
+
+def bf16_bits_t(t):
+    return t.view(torch.int16)
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 128, 128), (17, 384, 256), (64, 2560, 4096)])
 def test_head_logits(M, K, N):
     d = dev()
