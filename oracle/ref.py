@@ -20,7 +20,8 @@
   correctness gate this stands in for is greedy decode matching token for
   token (X post, section "FP8 only works if quality survives").  bf16
   roundings happen exactly where the GPU path rounds: the normalised input
-  of each block, each block output and the head input.
+  of each block, each block output and the head input; the residual stream
+  is held in fp32 (each residual add rounds to fp32), as on the GPU.
 
 Every matmul here is numpy's float64 matmul on dequantized (exact) values.
 """
@@ -103,11 +104,20 @@ def rmsnorm(h, eps=RMS_EPS):
     return h / np.sqrt(np.mean(h * h, axis=1, keepdims=True) + eps)
 
 
-def stack_layer(h, qg, qu, qd, eps=RMS_EPS):
-    """One pre-norm residual block: h + bf16(MLP(bf16(RMSNorm(h))))."""
+def block_output(h, qg, qu, qd, eps=RMS_EPS):
+    """The residual branch of one pre-norm block: bf16(MLP(bf16(RMSNorm(h))))."""
     xl = to_bf16(rmsnorm(h, eps))
-    y = to_bf16(swiglu_mlp(xl, qg, qu, qd))
-    return h + y
+    return to_bf16(swiglu_mlp(xl, qg, qu, qd))
+
+
+def residual_add(h, y):
+    """h + y rounded to fp32 (the residual stream is fp32)."""
+    return (np.asarray(h, dtype=np.float64) + np.asarray(y, dtype=np.float64)).astype(np.float32).astype(np.float64)
+
+
+def stack_layer(h, qg, qu, qd, eps=RMS_EPS):
+    """One pre-norm residual block: fl32(h + bf16(MLP(bf16(RMSNorm(h)))))."""
+    return residual_add(h, block_output(h, qg, qu, qd, eps))
 
 
 def head_logits(h, w_head):

@@ -3,6 +3,7 @@ integer arithmetic, identity-quantization special cases, closed forms and
 brute-force loops."""
 
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -189,7 +190,7 @@ def test_stack_layer_and_head_rounding_points():
     h1 = ref.stack_layer(h, *q)
     xl = fp8.to_bf16(ref.rmsnorm(h))
     y = fp8.to_bf16(ref.swiglu_mlp(xl, *q))
-    assert np.array_equal(h1, h + y)
+    assert np.array_equal(h1, (h + y).astype(np.float32).astype(np.float64))
     assert np.array_equal(fp8.to_bf16(y), y)
     head = _bf16(rng, (V, d), 0.02)
     lg = ref.head_logits(h1, head)
@@ -206,3 +207,60 @@ def test_error_metrics():
     assert ref.rel_fro(r, r) == 0.0
     assert ref.rel_fro(np.array([[3.0, 4.0 + 5.0]]), r) == 1.0
     assert ref.max_abs_ratio(np.array([[3.0, 4.4]]), r) == pytest.approx(0.1)
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked decode-stack examples (tests/golden/stack_worked_example.txt,
+# which derives every value in its comments)
+# ---------------------------------------------------------------------------
+def _golden(name):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = [float(t) for t in v.split()]
+    return vals
+
+
+def test_stack_layer_worked_example():
+    g = _golden("stack_worked_example.txt")
+    x = np.empty(128)
+    x[0:4] = 1.75
+    x[4:117] = [(-1.0) ** i for i in range(4, 117)]
+    x[117:] = 0.5
+    h = (2.0 * x)[None, :]
+    wg = np.zeros((128, 128))
+    wg[np.arange(127), np.arange(127)] = 1.0
+    wg[127, 127] = 448.0
+    wg[0, 5] = 0.25
+    wu = np.zeros((128, 128))
+    wu[0, 3] = 448.0
+    wd = np.zeros((128, 128))
+    wd[0:5, 0] = [448.0, 1.0, -0.5, 2.0 ** -9, -3.5]
+    out = ref.stack_layer(h, *(ref.QWeight(w, "block") for w in (wg, wu, wd)), eps=0.0)
+    assert out[0, :5].tolist() == g["ex1_h_out_0_4"]
+    assert np.array_equal(out[0, 5:], h[0, 5:])
+
+
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+def test_stack_layer_zero_weights_rounds_the_residual_to_fp32(fmt):
+    g = _golden("stack_worked_example.txt")
+    h = np.ones((1, 128))
+    h[0, :4] = [1.0 + 2.0 ** -30, 3.0 + 2.0 ** -24, -(2.0 + 3.0 * 2.0 ** -23), 0.75 * 2.0 ** -149]
+    z = [ref.QWeight(np.zeros(s), fmt) for s in ((128, 128), (128, 128), (128, 128))]
+    out = ref.stack_layer(h, *z)
+    assert out[0, :4].tolist() == g["ex2_h_out_0_3"]
+    assert np.array_equal(out[0, 4:], h[0, 4:])
+
+
+def test_head_logits_worked_example():
+    g = _golden("stack_worked_example.txt")
+    h = np.array([[1.0 + 2.0 ** -9, 1.0 + 3.0 * 2.0 ** -8, -(2.0 + 2.0 ** -7), 0.5],
+                  [2.0 ** -130, 7.0, 255.5, 1.0 / 3.0]])
+    w = np.array([[1.0, 0, 0, 0], [1, 1, 1, 1], [0.5, -1, 2, 3], [0, 2, 0, 0]])
+    lg = ref.head_logits(h, w)
+    assert lg[0].tolist() == g["ex3_logits_0"]
+    assert lg[1].tolist() == g["ex3_logits_1"]
+    assert ref.argmax_rows(lg).tolist() == [int(v) for v in g["ex3_argmax"]]
