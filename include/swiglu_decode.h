@@ -33,7 +33,8 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously; nothing synchronises the host.
  *   - The library never allocates or frees memory and keeps no per-call
- *     global state, so calls can be captured into a hipGraph.
+ *     global state (its one process-wide setting is the wait budget below),
+ *     so calls can be captured into a hipGraph.
  *   - Errors detected on the host (bad argument, shape, alignment, size)
  *     are returned as a negative sgd_status and NOTHING is launched.  A
  *     launch failure returns SGD_EHIP.  Faults inside a kernel surface on
@@ -59,7 +60,8 @@ enum {
   SGD_EDIM = -3,       /* a dimension is not a multiple of its tile size    */
   SGD_EWORKSPACE = -4, /* workspace missing or smaller than required        */
   SGD_EFMT = -5,       /* unknown format, or operands of different formats  */
-  SGD_EHIP = -6        /* the HIP runtime refused a launch or a query       */
+  SGD_EHIP = -6,       /* the HIP runtime refused a launch or a query       */
+  SGD_ETIMEOUT = -7    /* a persistent kernel's wait gave up (see below)    */
 };
 
 /* ---- formats ----------------------------------------------------------- */
@@ -99,7 +101,9 @@ int sgd_abi_version(void);
 
 /* ---- sizes ------------------------------------------------------------- */
 /* Bytes of the packed codes / packed scales of an N x K weight; 0 if the
- * format or a dimension is invalid (N, K must be positive multiples of 128). */
+ * format or a dimension is invalid.  Every weight of this library has N and
+ * K positive multiples of 128, each at most 2^20, and N*K < 2^31 (the
+ * streaming kernels address a weight with 32-bit offsets). */
 size_t sgd_packed_codes_bytes(int fmt, int N, int K);
 size_t sgd_packed_scales_bytes(int fmt, int N, int K);
 
@@ -112,8 +116,8 @@ size_t sgd_packed_scales_bytes(int fmt, int N, int K);
  * section "Estrategia de cuantización FP8" (128x128 block and 1x32 UE8M0
  * microscaling) and the X post section "Custom kernels for the shapes TTS
  * actually uses".  The output is bit-identical to the plain definition.
- * Errors: SGD_EFMT, SGD_EINVAL (null, N/K <= 0), SGD_EDIM (N or K not a
- * multiple of 128), SGD_EALIGN.
+ * Errors: SGD_EFMT, SGD_EINVAL (null, N/K <= 0 or > 2^20), SGD_EDIM (N or K
+ * not a multiple of 128, or N*K >= 2^31), SGD_EALIGN.
  */
 int sgd_quantize_pack_weight(int fmt, const uint16_t* w_bf16, int N, int K,
                              void* codes_out, void* scales_out, void* stream);
@@ -146,20 +150,60 @@ int sgd_quantize_act(int fmt, const uint16_t* x_bf16, int M, int K,
  * kernel); every call that completes leaves it ready for the next (counters
  * zero, flags holding the number of the launch that raised them), so one
  * workspace can serve calls of any shape that fit in it.  After a call that
- * did not complete (a device fault), clear it again.  Calls that share a workspace
- * must not overlap (serialise them on one stream).  Size in bytes; 0 on
- * invalid arguments or when the shape needs more counters than the control
- * block holds (the output width N, or d of the MLP, must be <= 860160).
- * The size does not depend on the device.  The kernels assume that all of
- * their workgroups can be resident at once (they size the grid so), so a
- * second persistent launch must not run concurrently on the same device.
+ * did not complete (a device fault, or SGD_ETIMEOUT from sgd_workspace_status),
+ * clear it again.  Calls that share a workspace must not overlap (serialise
+ * them on one stream).  Size in bytes; 0 on invalid arguments (weight limits
+ * as for sgd_packed_codes_bytes; ffn <= 32768 for the MLP).  The size does
+ * not depend on the device.
+ *
+ * Persistent kernels.  sgd_scaled_gemm and sgd_fused_swiglu_mlp launch one
+ * workgroup per compute unit, and their workgroups wait for each other, so
+ * all of them must be resident at once: do not run a second such launch (or
+ * any kernel that holds compute units for long) concurrently on the same
+ * device.  Every wait is bounded: one that spins longer than the wait budget
+ * gives up, the launch then runs to its end without waiting (its outputs are
+ * invalid) and the workspace records the failure, which
+ * sgd_workspace_status reports.
  */
 size_t sgd_gemm_workspace_bytes(int fmt, int M, int N, int K);
 size_t sgd_mlp_workspace_bytes(int fmt, int M, int d, int ffn);
 
+/*
+ * Where sgd_fused_swiglu_mlp keeps its intermediates in the workspace, for
+ * inspection and tests (the layout belongs to this ABI version).  Writes
+ * five byte offsets into `offsets` (host array of 5):
+ *   [0] Q(x) codes, [1] Q(x) scales, [2] a = silu(g)*u, fp32 [M, ffn]
+ *   row-major, [3] Q(a) codes, [4] Q(a) scales.
+ * Codes are stored m-tile by m-tile: rows 16t..16t+Mt-1 (Mt = min(16,
+ * M-16t)) form K/16 segments of 16 columns, each segment the Mt rows' 16
+ * codes in row order (K = d for Q(x), ffn for Q(a)).  BLOCK128 scales: fp32
+ * [K/128][Mpad] (Mpad = M rounded up to 16, 32, 64 or 128; padded rows
+ * zero).  MX32 scales: m-tile t holds, per 128-column k-tile, the Mt rows'
+ * four E8M0 bytes (one dword per row, 32-column blocks in order).  Q(x) is
+ * written to the workspace only when it does not fit in LDS (in practice
+ * M > 32, or a very wide d); a, Q(a) always.  Returns SGD_OK or
+ * SGD_EINVAL (shape or format invalid, or offsets NULL).
+ */
+int sgd_mlp_workspace_layout(int fmt, int M, int d, int ffn, size_t* offsets);
+
 /* Zero-fill `bytes` bytes of `workspace` with a fill kernel (no memset
  * node, so it is safe to capture).  bytes must be a multiple of 16. */
 int sgd_workspace_clear(void* workspace, size_t bytes, void* stream);
+
+/* Set the wait budget of the persistent kernels: the longest any one of
+ * their cross-workgroup waits may spin before the launch gives up, in
+ * microseconds (0 restores the default of 1 s).  A process-wide setting read
+ * when a call is launched (a captured graph keeps the value of its capture).
+ * Returns the previous budget. */
+uint32_t sgd_set_wait_budget_us(uint32_t us);
+
+/* Whether any launch on `workspace` gave up a wait since the workspace was
+ * last cleared: SGD_OK, or SGD_ETIMEOUT (then the outputs of the call(s)
+ * concerned are invalid; clear the workspace before reusing it).
+ * SYNCHRONISES `stream` and reads one word of the control block to the host,
+ * so it is a diagnostic, not for graph capture.  Errors: SGD_EINVAL (null),
+ * SGD_EALIGN, SGD_EHIP. */
+int sgd_workspace_status(const void* workspace, void* stream);
 
 /* ---- the hot path ------------------------------------------------------ */
 /*

@@ -20,6 +20,7 @@ __all__ = [
     "fmt_code", "quantize_pack_weight", "unpack_weight", "quantize_act", "scaled_gemm",
     "fused_swiglu_mlp", "bf16_to_f32", "rmsnorm_bf16", "residual_add", "head_logits",
     "argmax_rows", "gemm_workspace_bytes", "mlp_workspace_bytes", "lib",
+    "workspace_status", "set_wait_budget_us",
 ]
 
 _FMTS = {"block": FMT_BLOCK128, "mx": FMT_MX32, FMT_BLOCK128: FMT_BLOCK128, FMT_MX32: FMT_MX32}
@@ -135,8 +136,9 @@ def mlp_workspace_bytes(fmt, M, d, ffn):
 class Workspace:
     """A zero-initialised device workspace that grows on demand.  The kernels
     leave its control block ready for the next call (counters zero, flags
-    holding the number of the launch that raised them); calls sharing one
-    workspace must be serialised on one stream."""
+    holding the number of the launch that raised them).  Calls that share a
+    workspace must not overlap; the binding orders them (see
+    _serialise_persistent), whatever stream each is issued on."""
 
     def __init__(self, device, nbytes=0):
         self.device = torch.device(device)
@@ -153,17 +155,80 @@ class Workspace:
         return self.tensor
 
 
+    def clear(self):
+        """Zero the whole workspace again (after SGD_ETIMEOUT or a fault)."""
+        if self.tensor is not None:
+            _lib.check("sgd_workspace_clear", lib().sgd_workspace_clear(
+                _ptr(self.tensor), self.tensor.numel(), _stream(self.tensor)))
+
+    def status(self):
+        """SGD_OK (0) or SGD_ETIMEOUT (-7): whether a launch on this workspace
+        gave up a wait since it was last cleared.  Synchronises the stream."""
+        if self.tensor is None:
+            return 0
+        st = lib().sgd_workspace_status(_ptr(self.tensor), _stream(self.tensor))
+        if st not in (0, _lib.SGD_ETIMEOUT):
+            _lib.check("sgd_workspace_status", st)
+        return st
+
+
+# One default workspace per device (not per stream): persistent launches on
+# one device must not overlap, whichever stream they are issued on.
 _DEFAULT_WS = {}
+# Per device: (stream handle, event) of the last persistent launch issued
+# through this binding.
+_LAST_LAUNCH = {}
 
 
 def _workspace(device, nbytes, ws):
     if ws is None:
-        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
-        ws = _DEFAULT_WS.get(key)
+        ws = _DEFAULT_WS.get(device.index)
         if ws is None:
-            ws = _DEFAULT_WS[key] = Workspace(device)
+            ws = _DEFAULT_WS[device.index] = Workspace(device)
     t = ws.ensure(nbytes)
     return t
+
+
+def _serialise_persistent(device, launch):
+    """Run `launch()` (one persistent-kernel call, with the sizing of its
+    workspace) so that it cannot overlap the previous persistent call on the
+    same device: when that one was issued on another stream, the current
+    stream first waits for it.  All workgroups of a persistent kernel must be
+    resident at once, so two of them running side by side could each hold
+    compute units the other waits for; and a workspace that grows must not be
+    freed under a call still running on another stream.  (Inside a graph
+    capture the captured stream's own order applies.)"""
+    stream = torch.cuda.current_stream(device)
+    capturing = torch.cuda.is_current_stream_capturing()
+    last = _LAST_LAUNCH.get(device.index)
+    if last is not None and not capturing and last[0] != stream.cuda_stream:
+        stream.wait_event(last[1])
+    out = launch()
+    if not capturing:
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        _LAST_LAUNCH[device.index] = (stream.cuda_stream, ev)
+    return out
+
+
+def workspace_status(ws):
+    """Status of a Workspace (see Workspace.status)."""
+    return ws.status()
+
+
+def set_wait_budget_us(us):
+    """Set the persistent kernels' wait budget in microseconds (0: default
+    1 s); returns the previous value.  Process-wide."""
+    return int(lib().sgd_set_wait_budget_us(int(us)))
+
+
+def mlp_workspace_layout(fmt, M, d, ffn):
+    """Byte offsets of the fused MLP's intermediates in its workspace:
+    dict(xq, xs, a, aq, as_) (layouts in swiglu_decode.h, for inspection)."""
+    off = (ctypes.c_size_t * 5)()
+    _lib.check("sgd_mlp_workspace_layout",
+               lib().sgd_mlp_workspace_layout(fmt_code(fmt), M, d, ffn, off))
+    return dict(zip(("xq", "xs", "a", "aq", "as_"), (int(v) for v in off)))
 
 
 def scaled_gemm(x, w, out=None, workspace=None):
@@ -180,10 +245,13 @@ def scaled_gemm(x, w, out=None, workspace=None):
     need = lib().sgd_gemm_workspace_bytes(w.fmt, M, w.N, w.K)
     if need == 0:
         raise ValueError(f"unsupported GEMM shape M={M} N={w.N} K={w.K}")
-    ws = _workspace(x.device, need, workspace)
     st = w.c_struct()
-    _lib.check("sgd_scaled_gemm", lib().sgd_scaled_gemm(
-        _ptr(x), M, ctypes.byref(st), _ptr(out), _ptr(ws), ws.numel(), _stream(x)))
+
+    def launch():
+        ws = _workspace(x.device, need, workspace)
+        _lib.check("sgd_scaled_gemm", lib().sgd_scaled_gemm(
+            _ptr(x), M, ctypes.byref(st), _ptr(out), _ptr(ws), ws.numel(), _stream(x)))
+    _serialise_persistent(x.device, launch)
     return out
 
 
@@ -201,11 +269,14 @@ def fused_swiglu_mlp(x, gate, up, down, out=None, workspace=None):
     need = lib().sgd_mlp_workspace_bytes(gate.fmt, M, d, gate.N)
     if need == 0:
         raise ValueError(f"unsupported MLP shape M={M} d={d} ffn={gate.N}")
-    ws = _workspace(x.device, need, workspace)
     g, u, dn = gate.c_struct(), up.c_struct(), down.c_struct()
-    _lib.check("sgd_fused_swiglu_mlp", lib().sgd_fused_swiglu_mlp(
-        _ptr(x), M, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), _ptr(out),
-        _ptr(ws), ws.numel(), _stream(x)))
+
+    def launch():
+        ws = _workspace(x.device, need, workspace)
+        _lib.check("sgd_fused_swiglu_mlp", lib().sgd_fused_swiglu_mlp(
+            _ptr(x), M, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), _ptr(out),
+            _ptr(ws), ws.numel(), _stream(x)))
+    _serialise_persistent(x.device, launch)
     return out
 
 

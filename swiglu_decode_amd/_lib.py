@@ -13,7 +13,8 @@ FMT_MX32 = 2
 MAX_M = 128
 
 STATUS = {0: "SGD_OK", -1: "SGD_EINVAL", -2: "SGD_EALIGN", -3: "SGD_EDIM",
-          -4: "SGD_EWORKSPACE", -5: "SGD_EFMT", -6: "SGD_EHIP"}
+          -4: "SGD_EWORKSPACE", -5: "SGD_EFMT", -6: "SGD_EHIP", -7: "SGD_ETIMEOUT"}
+SGD_ETIMEOUT = -7
 
 
 class SgdWeight(ctypes.Structure):
@@ -54,6 +55,9 @@ SIGNATURES = {
     "sgd_head_logits": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
     "sgd_argmax_rows": (_i, [_vp, _i, _i, _vp, _vp]),
     "sgd_read_stream": (_i, [_vp, _sz, _vp, _vp]),
+    "sgd_set_wait_budget_us": (ctypes.c_uint32, [ctypes.c_uint32]),
+    "sgd_workspace_status": (_i, [_vp, _vp]),
+    "sgd_mlp_workspace_layout": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
 }
 
 _LIB = None

@@ -4,22 +4,33 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 using namespace sgd;
 
 namespace {
 
-constexpr int ABI_VERSION = 1;
+constexpr int ABI_VERSION = 2;
 constexpr int MAX_DIM = 1 << 20;
+// The streaming kernels address a weight's codes with 32-bit offsets and use
+// offset 2^31 as their past-the-end filler, so a weight holds fewer than 2^31
+// codes.
+constexpr size_t MAX_WEIGHT_BYTES = size_t(1) << 31;
+// The persistent kernels' wait budget (sgd_set_wait_budget_us).
+constexpr uint32_t DEFAULT_WAIT_BUDGET_US = 1000000;
+std::atomic<uint32_t> g_wait_budget_us{DEFAULT_WAIT_BUDGET_US};
 
 inline bool fmt_ok(int fmt) { return fmt == SGD_FMT_BLOCK128 || fmt == SGD_FMT_MX32; }
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-// N, K of a weight: positive multiples of 128 within range.
+// N, K of a weight: positive multiples of 128 within range, fewer than 2^31
+// elements in all.
 int check_nk(int N, int K) {
   if (N <= 0 || K <= 0 || N > MAX_DIM || K > MAX_DIM) return SGD_EINVAL;
   if ((N % 128) || (K % 128)) return SGD_EDIM;
+  if ((size_t)N * (size_t)K >= MAX_WEIGHT_BYTES) return SGD_EDIM;
   return SGD_OK;
 }
 
@@ -36,6 +47,10 @@ int check_weight(const sgd_weight* w) {
 
 }  // namespace
 
+namespace sgd {
+uint64_t wait_budget_ticks() { return (uint64_t)g_wait_budget_us.load(std::memory_order_relaxed) * 100u; }
+}  // namespace sgd
+
 extern "C" {
 
 const char* sgd_status_str(int status) {
@@ -47,6 +62,9 @@ const char* sgd_status_str(int status) {
     case SGD_EWORKSPACE: return "workspace missing or too small";
     case SGD_EFMT: return "unknown format or mixed formats";
     case SGD_EHIP: return "HIP runtime error";
+    case SGD_ETIMEOUT:
+      return "a cross-workgroup wait of a persistent kernel gave up (workgroups not resident at once); "
+             "outputs of that call are invalid and the workspace must be cleared";
     default: return "unknown status";
   }
 }
@@ -105,10 +123,34 @@ size_t sgd_mlp_workspace_bytes(int fmt, int M, int d, int ffn) {
   return stream_workspace_bytes(fmt, M, d, ffn, d, ffn, true);
 }
 
+int sgd_mlp_workspace_layout(int fmt, int M, int d, int ffn, size_t* offsets) {
+  if (!offsets || sgd_mlp_workspace_bytes(fmt, M, d, ffn) == 0) return SGD_EINVAL;
+  size_t off[5];
+  const int rc = stream_workspace_layout(fmt, M, d, ffn, off);
+  if (rc != SGD_OK) return rc;
+  for (int i = 0; i < 5; ++i) offsets[i] = off[i];
+  return SGD_OK;
+}
+
 int sgd_workspace_clear(void* workspace, size_t bytes, void* stream) {
   if (!workspace || bytes == 0) return SGD_EINVAL;
   if (!al16(workspace) || (bytes % 16)) return SGD_EALIGN;
   return launch_fill_zero(workspace, bytes, as_stream(stream));
+}
+
+uint32_t sgd_set_wait_budget_us(uint32_t us) {
+  return g_wait_budget_us.exchange(us == 0 ? DEFAULT_WAIT_BUDGET_US : us, std::memory_order_relaxed);
+}
+
+int sgd_workspace_status(const void* workspace, void* stream) {
+  if (!workspace) return SGD_EINVAL;
+  if (!al16(workspace)) return SGD_EALIGN;
+  if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return SGD_EHIP;
+  uint32_t gave_up = 0;
+  if (hipMemcpy(&gave_up, static_cast<const uint32_t*>(workspace) + CTRL_ERR_WORD, sizeof(gave_up),
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return SGD_EHIP;
+  return gave_up ? SGD_ETIMEOUT : SGD_OK;
 }
 
 int sgd_read_stream(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

@@ -32,6 +32,9 @@ struct Problem {
   void* ws;
 };
 size_t stream_workspace_bytes(int fmt, int M, int K1, int F, int N, int K2, bool mlp);
+// Byte offsets of the fused MLP's workspace regions: Q(x) codes, Q(x)
+// scales, a (fp32), Q(a) codes, Q(a) scales.
+int stream_workspace_layout(int fmt, int M, int K1, int F, size_t (&off)[5]);
 int launch_stream(const Problem& p, hipStream_t s);
 
 // Decode-stack glue.
@@ -41,6 +44,15 @@ int launch_residual_add(float* h, const uint16_t* y, int M, int d, hipStream_t s
 int launch_residual_rmsnorm(float* h, const uint16_t* y, int M, int d, float eps, uint16_t* x, hipStream_t s);
 int launch_head(const float* h, int M, int K, const uint16_t* w, int N, float* out, hipStream_t s);
 int launch_argmax(const float* logits, int M, int N, int32_t* out, hipStream_t s);
+
+// Word of the workspace control block that counts waits that gave up
+// (sticky until the workspace is cleared).
+constexpr int CTRL_ERR_WORD = 65;
+
+// Longest a cross-workgroup wait of the persistent kernels may spin before
+// the launch gives up (sgd_set_wait_budget_us), in ticks of the device's
+// 100 MHz real-time counter.
+uint64_t wait_budget_ticks();
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? SGD_OK : SGD_EHIP; }
 

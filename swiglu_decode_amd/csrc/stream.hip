@@ -119,6 +119,7 @@ struct Args {
   int n_pairs, n_items;      // x quantization: (k-group, row tile) pairs, dealt into items
   int ngroups;               // F / 128
   int ks;                    // gate/up with LDS-staged activations (Cfg::KS variants)
+  uint64_t budget;           // longest a wait may spin, in ticks of the 100 MHz real-time counter
   Phase gu, dn;
 };
 
@@ -130,6 +131,12 @@ constexpr int C_DONE = 0;
 // clearing; every counter is zeroed by its own last arriver.  The last
 // workgroup then only advances C_EPOCH and zeroes C_DONE.
 constexpr int C_EPOCH = 64;
+// A wait that spins longer than Args::budget gives up: it adds one to C_ERR
+// (sticky until the workspace is cleared; the host reads it) and stores the
+// launch number in C_ERR_EP, which ends every other wait of that launch at
+// once.  The launch then runs to its end on whatever data it has, so every
+// wavefront exits normally; its outputs are invalid.
+constexpr int C_ERR = CTRL_ERR_WORD, C_ERR_EP = CTRL_ERR_WORD + 1;
 constexpr int PAGE0 = 1024, PAGE_WORDS = 1024, NREP = 8;
 constexpr int PG_XQ = 0, PG_RDY = 512;
 constexpr int C_GCNT = PAGE0 + NREP * PAGE_WORDS;  // arrivals of 16-column bands per group
@@ -217,6 +224,7 @@ struct Lds {
   uint32_t a_ready;                // staged gate/up: k-tiles of Q(x) staged so far
   uint32_t prog[NS];               // staged gate/up: k-tiles each streaming wavefront has used
   uint32_t gu_left;                // streaming wavefronts done with gate/up (band finishing included)
+  uint32_t abort;                  // a wait of this workgroup gave up: every other wait ends at once
 };
 
 __device__ __forceinline__ uint32_t lds_load(const uint32_t* p) {
@@ -225,8 +233,52 @@ __device__ __forceinline__ uint32_t lds_load(const uint32_t* p) {
 __device__ __forceinline__ void lds_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_wait_geq(const uint32_t* p, uint32_t target) {
-  while (lds_load(p) < target) __builtin_amdgcn_s_sleep(1);
+// ---------------------------------------------------------------------------
+// Bounded waiting.  Every spin of the kernel carries a Guard: the
+// workgroup's LDS abort word and the launch's budget.  A wait whose budget
+// runs out (workgroups that are not all resident at once, e.g. beside another
+// persistent launch) gives up: it records the failure in the control block
+// (C_ERR, C_ERR_EP) and in the abort word, and returns.  After that every
+// wait of the workgroup, and every cross-workgroup wait of the launch,
+// returns at once, so the kernel always runs to its end.
+// ---------------------------------------------------------------------------
+struct Guard {
+  uint32_t* abort;  // LDS
+  uint32_t* ctrl;
+  uint64_t budget;  // ticks of the 100 MHz real-time counter
+  uint32_t ep;      // this launch's number
+};
+
+__device__ __forceinline__ void give_up(const Guard& g) {
+  if (lane_id() == 0) {
+    lds_store(g.abort, 1u);
+    atomic_add_agent(g.ctrl + C_ERR, 1u);
+    store_agent(g.ctrl + C_ERR_EP, g.ep);
+  }
+}
+
+// Checked every 16th pass of a spin that polls LDS: true when the wait must
+// end (the workgroup gave up, or this wait outlived the budget; t0 is taken
+// on the first check).
+__device__ __forceinline__ bool must_stop(const Guard& g, uint32_t& pass, uint64_t& t0) {
+  if ((++pass & 15u) != 0u) return false;
+  if (lds_load(g.abort)) return true;
+  const uint64_t t = wall_clock64();
+  if (t0 == 0) t0 = t;
+  if (t - t0 > g.budget) {
+    give_up(g);
+    return true;
+  }
+  return false;
+}
+
+__device__ __forceinline__ void lds_wait_geq(const Guard& g, const uint32_t* p, uint32_t target) {
+  uint32_t pass = 0;
+  uint64_t t0 = 0;
+  while (lds_load(p) < target) {
+    if (must_stop(g, pass, t0)) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -269,6 +321,7 @@ struct Streamer {
   const Args& a;
   const int q;  // index among the workgroup's streaming wavefronts
   const uint8_t* lx;  // LDS copy of Q(x) (XL)
+  const Guard gd;
   // buffer resources of the current phase
   __amdgpu_buffer_rsrc_t rw0, rw1, rs0, rs1, rx, rxs;
   // lane constants
@@ -277,7 +330,8 @@ struct Streamer {
   uint32_t xsh;                    // mx gate/up: bit offset of this lane's first block scale in X0
   uint32_t xs_lane;                // block format: activation-scale lane offset (bytes)
 
-  __device__ Streamer(const Args& args, int wq, const uint8_t* lds_x) : a(args), q(wq), lx(lds_x) {
+  __device__ Streamer(const Args& args, int wq, const uint8_t* lds_x, const Guard& g)
+      : a(args), q(wq), lx(lds_x), gd(g) {
     const int l = lane_id();
     lo16 = (uint32_t)l * 16u;
     mo_gu0 = ((uint32_t)(l & 15) + 16u * (uint32_t)((l >> 4) >> 1)) * 4u;
@@ -595,7 +649,7 @@ struct Streamer {
     for (int s = 0; s < 2; ++s) load_b<true>(R, s, cp, KT, s);
     // the rest once Q(x) exists: a full prefetch at launch would delay the
     // x quantization and its cross-workgroup flags (measured)
-    lds_wait_geq(&L.xq_ok, 1u);
+    lds_wait_geq(gd, &L.xq_ok, 1u);
 #pragma unroll
     for (int s = 2; s < PG; ++s) load_b<true>(R, s, cp, KT, s);
     v4f acc[2][MT];
@@ -608,7 +662,7 @@ struct Streamer {
       for (int s = 0; s < PG; ++s) {
         const int kt = k0 + s;
         if (kt < KT) {
-          lds_wait_geq(&L.a_ready, (uint32_t)(kt + 1));
+          lds_wait_geq(gd, &L.a_ready, (uint32_t)(kt + 1));
           step_gu_staged(R, s, kt, stages + (kt % DA) * SB, acc);
           if (lane_id() == 0) lds_store(&L.prog[q], (uint32_t)(kt + 1));
         }
@@ -621,19 +675,24 @@ struct Streamer {
   // Wait until the groups of Q(a) that chunk cp reads are ready (its k-tiles
   // lie in one word of the mask: PP divides 32 and k-tiles start at multiples of PP).
   template <int PP, int NS, int NSLOT>
-  static __device__ __forceinline__ void wait_groups(Lds<MT, NS, NSLOT>& L, const ChunkPos& cp, int KT) {
+  __device__ __forceinline__ void wait_groups(Lds<MT, NS, NSLOT>& L, const ChunkPos& cp, int KT) const {
     if (!cp.ok) return;
     const int n = min(PP, KT - cp.kt0);
     const uint32_t need = ((1u << n) - 1u) << (cp.kt0 & 31);
     const uint32_t* w = &L.rdy[cp.kt0 >> 5];
-    while ((lds_load(w) & need) != need) __builtin_amdgcn_s_sleep(1);
+    uint32_t pass = 0;
+    uint64_t t0 = 0;
+    while ((lds_load(w) & need) != need) {
+      if (must_stop(gd, pass, t0)) return;
+      __builtin_amdgcn_s_sleep(1);
+    }
   }
 
   // Hand this wavefront's sums for band event k to the sync wavefront.
   template <int NS, int NSLOT>
   __device__ __forceinline__ void publish(Lds<MT, NS, NSLOT>& L, int k, v4f (&acc)[2][MT]) {
     const int slot = k % NSLOT;
-    if (k >= NSLOT) lds_wait_geq(&L.consumed, (uint32_t)(k - NSLOT + 1));
+    if (k >= NSLOT) lds_wait_geq(gd, &L.consumed, (uint32_t)(k - NSLOT + 1));
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -667,7 +726,7 @@ struct Streamer {
     // activations only once they exist (the LDS copy of Q(x) already does;
     // Q(a) chunk by chunk, as its groups become ready)
     if (PK != PK_DN) {
-      if (!XL) lds_wait_geq(&L.xq_ok, 1u);
+      if (!XL) lds_wait_geq(gd, &L.xq_ok, 1u);
     } else {
       wait_groups<PP>(L, cp, KT);
     }
@@ -941,13 +1000,33 @@ __device__ __forceinline__ void raise_flag(uint32_t* ctrl, int page_off, int i, 
   if (l < NREP) store_agent(&ctrl[PAGE0 + l * PAGE_WORDS + page_off + i], ep);
 }
 
+// A cross-workgroup wait has lasted one more pass: true when it must end
+// (some wait of this launch gave up, as err_ep shows, or this one outlived the
+// budget).
+__device__ __forceinline__ bool must_stop_global(const Guard& g, uint32_t err_ep, uint64_t& t0) {
+  if (err_ep == g.ep) {
+    if (lane_id() == 0) lds_store(g.abort, 1u);
+    return true;
+  }
+  const uint64_t t = wall_clock64();
+  if (t0 == 0) t0 = t;
+  if (t - t0 > g.budget) {
+    give_up(g);
+    return true;
+  }
+  return false;
+}
+
 // Spin until flags [0, n) of this XCD's copy are all raised in this launch.
-__device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_t ep) {
+__device__ __forceinline__ void wait_flags(const Guard& g, const uint32_t* flags, int n) {
   const int l = lane_id();
+  uint64_t t0 = 0;
   for (;;) {
     bool ok = true;
-    for (int i = l; i < n; i += 64) ok = ok && load_agent(flags + i) == ep;
+    for (int i = l; i < n; i += 64) ok = ok && load_agent(flags + i) == g.ep;
+    const uint32_t err_ep = load_agent(g.ctrl + C_ERR_EP);
     if (__all(ok)) break;
+    if (must_stop_global(g, err_ep, t0)) break;
     __builtin_amdgcn_s_sleep(8);
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -957,16 +1036,18 @@ __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_
 // each 32-group word into the workgroup's LDS mask as its flags rise (flags
 // only rise during a launch, so every copy only adds bits).
 template <int MT, int NS, int NSLOT>
-__device__ __forceinline__ void mirror_ready(Lds<MT, NS, NSLOT>& L, const uint32_t* flags, int g0, int g1,
-                                             uint32_t ep) {
+__device__ __forceinline__ void mirror_ready(const Guard& gd, Lds<MT, NS, NSLOT>& L, const uint32_t* flags, int g0,
+                                             int g1) {
   const int l = lane_id();
   const int a0 = g0 & ~31;
+  uint64_t t0 = 0;
   for (;;) {
     bool all = true;
+    const uint32_t err_ep = load_agent(gd.ctrl + C_ERR_EP);
     for (int i0 = a0; i0 < g1; i0 += 64) {
       const int i = i0 + l;
       const bool in = i >= g0 && i < g1;
-      const bool r = in && load_agent(flags + i) == ep;
+      const bool r = in && load_agent(flags + i) == gd.ep;
       const uint64_t bal = __ballot(r);
       all = all && __all(r || !in);
       if (l == 0) {
@@ -975,6 +1056,7 @@ __device__ __forceinline__ void mirror_ready(Lds<MT, NS, NSLOT>& L, const uint32
       }
     }
     if (all) break;
+    if (must_stop_global(gd, err_ep, t0)) break;
     __builtin_amdgcn_s_sleep(4);
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1070,9 +1152,9 @@ __device__ __forceinline__ bool arrive_shared(const Args& a, const Phase& ph, fl
 }
 
 template <int MT, int NS, int NSLOT>
-__device__ __forceinline__ void take_event(Lds<MT, NS, NSLOT>& L, int k, v4f (&s)[2][MT]) {
+__device__ __forceinline__ void take_event(const Guard& gd, Lds<MT, NS, NSLOT>& L, int k, v4f (&s)[2][MT]) {
   const int slot = k % NSLOT;
-  lds_wait_geq(&L.arrived[slot], (uint32_t)NS);
+  lds_wait_geq(gd, &L.arrived[slot], (uint32_t)NS);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -1143,7 +1225,8 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
 // Stage kt % DA is rewritten once every one of them has used k-tile kt - DA;
 // LD k-tiles are in flight in registers.
 template <int MT, int FMT, int NS, int NSLOT>
-__device__ __forceinline__ void stage_activations(const Args& a, Lds<MT, NS, NSLOT>& L, uint8_t* stages, int nst) {
+__device__ __forceinline__ void stage_activations(const Guard& gd, const Args& a, Lds<MT, NS, NSLOT>& L,
+                                                  uint8_t* stages, int nst) {
   constexpr int DA = Cfg<MT>::DA, SB = ks_stage_bytes<MT>(), LD = 2;
   const int l = lane_id();
   const uint32_t r = (uint32_t)(l & 15), g = (uint32_t)(l >> 4);
@@ -1198,7 +1281,7 @@ __device__ __forceinline__ void stage_activations(const Args& a, Lds<MT, NS, NSL
       const int kt = k0 + u;
       if (kt < KT) {
         if (kt >= DA)
-          for (int w = 0; w < nst; ++w) lds_wait_geq(&L.prog[w], (uint32_t)(kt - DA + 1));
+          for (int w = 0; w < nst; ++w) lds_wait_geq(gd, &L.prog[w], (uint32_t)(kt - DA + 1));
         write(u, kt);
         if (l == 0) lds_store(&L.a_ready, (uint32_t)(kt + 1));
       }
@@ -1214,6 +1297,7 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
   const int rep = W & (NREP - 1);
   const uint32_t* page = a.ctrl + PAGE0 + rep * PAGE_WORDS;
   const uint32_t ep = launch_epoch(a);
+  const Guard gd{&L.abort, a.ctrl, a.budget, ep};
   if (!XL) {
     // quantize this workgroup's share of x, then wait for everyone's
     if (W < a.n_items) {
@@ -1221,7 +1305,7 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
       drain_memory();
       raise_flag(a.ctrl, PG_XQ, W, ep);
     }
-    wait_flags(page + PG_XQ, a.n_items, ep);
+    wait_flags(gd, page + PG_XQ, a.n_items);
     if (l == 0) lds_store(&L.xq_ok, 1u);
   }
 
@@ -1232,11 +1316,11 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
     if (Cfg<MT>::KS && a.ks) {
       // the streaming wavefronts finish their own bands
       const int nst = min((c1 - c0) / ph.CPB, NS);
-      if (nst > 0) stage_activations<MT, FMT>(a, L, stages, nst);
+      if (nst > 0) stage_activations<MT, FMT>(gd, a, L, stages, nst);
     } else if (c0 < c1) {
       for (int b = c0 / ph.CPB; b <= (c1 - 1) / ph.CPB; ++b) {
         v4f s[2][MT];
-        take_event(L, k++, s);
+        take_event(gd, L, k++, s);
         finish_gu_band<MT, FMT>(a, b, s, ep);
       }
     }
@@ -1252,11 +1336,11 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
           g0 = (c0 % ph.CPB) * Cfg<MT>::PD;
           g1 = min(ph.KT, ((c1 - 1) % ph.CPB) * Cfg<MT>::PD + Cfg<MT>::PD);
         }
-        mirror_ready(L, page + PG_RDY, g0, g1, ep);
+        mirror_ready(gd, L, page + PG_RDY, g0, g1);
       }
       for (int b = c0 / ph.CPB; b <= (c1 - 1) / ph.CPB; ++b) {
         v4f s[2][MT];
-        take_event(L, k++, s);
+        take_event(gd, L, k++, s);
         finish_dn_band<MT>(a, b, s);
       }
     }
@@ -1265,7 +1349,7 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
   // variant they finish bands themselves, and those flag and counter updates
   // must precede this workgroup's arrival); the last workgroup advances the
   // launch number
-  if (a.mlp) lds_wait_geq(&L.gu_left, (uint32_t)NS);
+  if (a.mlp) lds_wait_geq(gd, &L.gu_left, (uint32_t)NS);
   drain_memory();
   uint32_t old = 0;
   if (l == 0) old = atomic_add_agent(&a.ctrl[C_DONE], 1u);
@@ -1275,6 +1359,7 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
     // the launch number is about to wrap: clear every flag (flags of earlier
     // launches could otherwise match a later number)
     for (int i = l; i < NREP * PAGE_WORDS; i += 64) store_agent(&a.ctrl[PAGE0 + i], 0u);
+    if (l == 0) store_agent(&a.ctrl[C_ERR_EP], 0u);
   }
   if (l == 0) {
     store_agent(&a.ctrl[C_EPOCH], ep == 0xFFFFFFFFu ? 0u : ep);
@@ -1303,6 +1388,7 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     L.a_ready = 0u;
     for (int i = 0; i < C::NS; ++i) L.prog[i] = 0u;
     L.gu_left = 0u;
+    L.abort = 0u;
   }
   __syncthreads();
   if (wv == 0) {
@@ -1314,7 +1400,8 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     }
     sync_wave<MT, FMT, XL>(a, L, lds_x);
   } else {
-    Streamer<MT, FMT, C::P, XL> st(a, wv - 1, lds_x);
+    const Guard gd{&L.abort, a.ctrl, a.budget, launch_epoch(a)};
+    Streamer<MT, FMT, C::P, XL> st(a, wv - 1, lds_x, gd);
     int k = 0;
     XqLocal<FMT> xq;
     if (XL) {
@@ -1535,6 +1622,17 @@ size_t stream_workspace_bytes(int fmt, int M, int K1, int F, int N, int K2, bool
   return p.ok ? p.bytes : 0;
 }
 
+int stream_workspace_layout(int fmt, int M, int K1, int F, size_t (&off)[5]) {
+  const Plan p = make_plan(fmt, M, K1, F, K1, F, true, MAX_WG);
+  if (!p.ok) return SGD_EDIM;
+  off[0] = p.off_xa;
+  off[1] = p.off_xs;
+  off[2] = p.off_a32;
+  off[3] = p.off_aq;
+  off[4] = p.off_as;
+  return SGD_OK;
+}
+
 int launch_stream(const Problem& pr, hipStream_t s) {
   const bool mlp = pr.gate != nullptr;
   const int F = mlp ? pr.gate->N : 0;
@@ -1580,6 +1678,7 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.n_items = XL ? 0 : p.n_items;
   a.ngroups = p.ngroups;
   a.ks = p.ks;
+  a.budget = wait_budget_ticks();
   a.gu = p.gu;
   a.dn = p.dn;
   void* args[] = {&a};

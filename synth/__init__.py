@@ -52,6 +52,8 @@ WORKLOADS = {
     "outlier": Workload("outlier", 5120, 13824, (64,), ("block", "mx"), 1004,
                         kind="outlier",
                         note="outlier stress d=5120, ffn=13824, M=64, both formats"),
+    "d2560": Workload("d2560", 2560, 9728, (1, 16, 64), ("block", "mx"), 1006,
+                      note="one decode-stack layer's MLP shape (d=2560, ffn=9728) at decode batch sizes"),
     "stack": Workload("stack", 2560, 9728, (64,), ("block",), 1005, kind="stack",
                       layers=24, vocab=4096,
                       note="24 pre-RMSNorm SwiGLU blocks + bf16 head, M=64"),

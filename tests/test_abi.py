@@ -10,7 +10,7 @@ import pytest
 from swiglu_decode_amd import _lib
 from swiglu_decode_amd._lib import SgdWeight
 
-E = dict(OK=0, EINVAL=-1, EALIGN=-2, EDIM=-3, EWORKSPACE=-4, EFMT=-5, EHIP=-6)
+E = dict(OK=0, EINVAL=-1, EALIGN=-2, EDIM=-3, EWORKSPACE=-4, EFMT=-5, EHIP=-6, ETIMEOUT=-7)
 BLK, MX = 1, 2
 
 
@@ -36,7 +36,7 @@ def test_status_strings_and_version(L):
     for code in E.values():
         assert L.sgd_status_str(code)
     assert b"unknown" in L.sgd_status_str(12345)
-    assert L.sgd_abi_version() == 1
+    assert L.sgd_abi_version() == 2
 
 
 def test_packed_sizes(L):
@@ -48,6 +48,12 @@ def test_packed_sizes(L):
     assert L.sgd_packed_codes_bytes(3, 256, 256) == 0
     assert L.sgd_packed_codes_bytes(BLK, 200, 256) == 0
     assert L.sgd_packed_codes_bytes(BLK, 0, 256) == 0
+    # a weight holds fewer than 2^31 codes (32-bit offsets in the streaming
+    # kernels), each dimension at most 2^20
+    assert L.sgd_packed_codes_bytes(BLK, 1 << 16, (1 << 15) - 128) == (1 << 16) * ((1 << 15) - 128)
+    assert L.sgd_packed_codes_bytes(BLK, 1 << 16, 1 << 15) == 0
+    assert L.sgd_packed_scales_bytes(MX, 1 << 20, 1 << 11) == 0
+    assert L.sgd_packed_codes_bytes(BLK, (1 << 20) + 128, 128) == 0
 
 
 def test_workspace_sizes(L):
@@ -95,6 +101,9 @@ def test_argument_errors_launch_nothing(L):
     assert L.sgd_scaled_gemm(P(0x1002), 4, ctypes.byref(w), P(0x1000), P(0x1000), ws_need, None) == E["EALIGN"]
     bad = _w(fmt=9)
     assert L.sgd_scaled_gemm(P(0x1000), 4, ctypes.byref(bad), P(0x1000), P(0x1000), ws_need, None) == E["EFMT"]
+    big = _w(N=1 << 16, K=1 << 15)  # 2^31 codes: past the 32-bit offsets
+    assert L.sgd_scaled_gemm(P(0x1000), 4, ctypes.byref(big), P(0x1000), P(0x1000), 1 << 40, None) == E["EDIM"]
+    assert L.sgd_quantize_pack_weight(BLK, P(0x1000), 1 << 16, 1 << 15, P(0x1000), P(0x1000), None) == E["EDIM"]
     # fused mlp: shapes must chain, formats must agree
     g, u, d = _w(N=512, K=256), _w(N=512, K=256), _w(N=256, K=512)
     need = L.sgd_mlp_workspace_bytes(BLK, 4, 256, 512)
@@ -103,6 +112,11 @@ def test_argument_errors_launch_nothing(L):
     assert args(g, u, _w(N=256, K=384)) == E["EDIM"]
     assert args(g, _w(fmt=MX, N=512, K=256), d) == E["EFMT"]
     assert args(g, u, d, need - 16) == E["EWORKSPACE"]
+    gb, ub, db = _w(N=1 << 15, K=1 << 16), _w(N=1 << 15, K=1 << 16), _w(N=1 << 16, K=1 << 15)
+    assert args(gb, ub, db, 1 << 40) == E["EDIM"]
+    # workspace status query: argument errors only (no GPU here)
+    assert L.sgd_workspace_status(None, None) == E["EINVAL"]
+    assert L.sgd_workspace_status(P(0x1004), None) == E["EALIGN"]
     # glue
     assert L.sgd_rmsnorm_bf16(P(0x1000), 4, 100, ctypes.c_float(1e-6), P(0x1000), None) == E["EDIM"]
     assert L.sgd_rmsnorm_bf16(P(0x1000), 4, 128, ctypes.c_float(-1.0), P(0x1000), None) == E["EINVAL"]
@@ -119,6 +133,14 @@ def test_argument_errors_launch_nothing(L):
     assert L.sgd_read_stream(P(0x1000), 1000, P(0x1000), None) == E["EALIGN"]
     assert L.sgd_read_stream(P(0x1008), 1024, P(0x1000), None) == E["EALIGN"]
     assert L.sgd_read_stream(P(0x1000), 1024, P(0x1002), None) == E["EALIGN"]
+
+
+def test_wait_budget_setting(L):
+    # process-wide; 0 restores the default (1 s); returns the previous value
+    prev = L.sgd_set_wait_budget_us(250)
+    assert L.sgd_set_wait_budget_us(0) == 250
+    assert L.sgd_set_wait_budget_us(prev) == 1000000
+    L.sgd_set_wait_budget_us(0)
 
 
 def test_binding_refuses_wrong_dtypes_without_gpu():

@@ -30,6 +30,40 @@ def test_scaled_gemm_parity(fmt, M, N, K):
     assert_close(gpu_out_f64(y), y_ref, f"gemm {fmt} M={M} {N}x{K}")
 
 
+_big = {}
+
+
+def _big_weight(N, K, fmt, d):
+    """One full-size weight at a time (bounded host memory): bf16, the
+    oracle's quantized copy and the packed GPU copy."""
+    key = (N, K, fmt)
+    if key not in _big:
+        _big.clear()
+        w = synth.random_bf16((N, K), 900 + N // 128 + K // 128, 0.02)
+        _big[key] = (w, oracle_weight(w, fmt), sgd.quantize_pack_weight(w.to(d), fmt))
+    return _big[key]
+
+
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+@pytest.mark.parametrize("N,K", [(12288, 4096), (4096, 12288)])
+@pytest.mark.parametrize("M", [1, 16, 64, 128])
+def test_scaled_gemm_full_size(fmt, N, K, M):
+    """The plain GEMM at the MLP's own shapes (gate/up: 12288 x 4096, down:
+    4096 x 12288): the second-GEMM bands are split over several workgroups and
+    combined (split-K) at every row-tile count."""
+    d = dev()
+    note(f"scaled_gemm full size {fmt} M={M} N={N} K={K}")
+    w, qw, pw = _big_weight(N, K, fmt, d)
+    x = synth.random_bf16((M, K), 21 + M, 1.0)
+    ws = sgd.Workspace(d, sgd.gemm_workspace_bytes(fmt, M, N, K))
+    y = sgd.scaled_gemm(x.to(d), pw, workspace=ws)
+    y2 = sgd.scaled_gemm(x.to(d), pw, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "a second call on the same workspace changed the result"
+    y_ref = ref.scaled_gemm(bf16_to_f64(x), qw)
+    assert_close(gpu_out_f64(y), y_ref, f"gemm {fmt} M={M} {N}x{K}")
+
+
 @pytest.mark.parametrize("fmt", ["block", "mx"])
 @pytest.mark.parametrize("M", [1, 5, 16, 33, 48, 64, 100, 128])
 @pytest.mark.parametrize("d_,F", [(256, 768), (512, 1536), (640, 1152)])
