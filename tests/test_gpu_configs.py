@@ -9,8 +9,10 @@ by every call):
 * d=5120, ffn=13824, M=64 with outlier activations and weights, both formats
   (the error against the unquantized MLP is reported per format);
 * the 24-layer pre-RMSNorm residual stack (d=2560, ffn=9728, M=64, block)
-  with a bf16 head, whose argmax must match the oracle on every row: expected
-  values written by tests/golden/make_stack_expected.py (oracle only).
+  with a bf16 head: argmax equal to the oracle's on every row after the
+  first block, and inside the spread of equally valid (perturbed-oracle)
+  results at every depth; expected values and the spread written by
+  tests/golden/make_stack_expected.py (oracle only).
 
 Every output element is compared (the oracle finishes these in seconds), and
 a second call on the same workspace must reproduce the first bit for bit."""
@@ -50,7 +52,12 @@ def _setup(name, fmt, d):
 CASES = [("tiny", "block", 1), ("tiny", "mx", 1),
          ("d2048", "block", 1), ("d2048", "block", 4), ("d2048", "block", 16),
          ("d4096", "mx", 1), ("d4096", "mx", 16), ("d4096", "mx", 64), ("d4096", "mx", 128),
-         ("outlier", "block", 64), ("outlier", "mx", 64)]
+         ("outlier", "block", 64), ("outlier", "mx", 64),
+         # widths whose gate/up bands are shared by two workgroups at one and
+         # two row tiles (the split-K combine of gate/up at M <= 32)
+         ("d2560", "block", 1), ("d2560", "block", 16), ("d2560", "mx", 1), ("d2560", "mx", 16),
+         ("d2560", "block", 64), ("d2560", "mx", 64),
+         ("outlier", "block", 1), ("outlier", "block", 16), ("outlier", "mx", 1), ("outlier", "mx", 16)]
 
 
 @pytest.mark.parametrize("name,fmt,M", CASES)
@@ -77,23 +84,44 @@ STACK_EXPECTED = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golde
                               "stack_d2560_ffn9728_m64_oracle.npz")
 
 
+def _stack_depth_stats(lg, exp, depth):
+    """Agreement with the oracle's argmax, relative logit error and largest
+    |difference| on the stored column subset, and the mismatching rows that
+    are not near-ties (oracle margin >= factor x that largest difference)."""
+    am = lg.argmax(axis=1)
+    am0 = exp["argmax"][depth]
+    sub = lg[:, exp["cols"]].astype(np.float64)
+    sub0 = exp["logits_sub"][depth].astype(np.float64)
+    maxdiff = float(np.max(np.abs(sub - sub0)))
+    mism = am != am0
+    nonnear = int(np.sum(mism & (exp["margin"][depth] >= float(exp["near_tie_factor"]) * maxdiff)))
+    return dict(agree=int(np.sum(~mism)), relerr=ref.rel_fro(sub, sub0), maxdiff=maxdiff, nonnear=nonnear,
+                bad=[(int(r), int(am[r]), int(am0[r]), float(exp["margin"][depth][r])) for r in np.nonzero(mism)[0]])
+
+
 @pytest.mark.timeout(600)
 def test_decode_stack_argmax():
     """The 24-block stack run end to end on the GPU (RMSNorm, fused MLP,
-    residual add; bf16 head and argmax after every block).
+    residual add; bf16 head and argmax after every block), against the
+    oracle and against the spread of equally valid results.
 
-    Strict at depth 1: every row's argmax equals the oracle's and the logits
-    agree to the MLP tolerance.  Deeper, the comparison is reported, not
-    asserted: with random N(0, 0.02) weights each block's output is as large
-    as the residual stream and fp8 quantization is discontinuous, so the stack
-    amplifies any difference in rounding order (a one-step bf16 change on 1 %
-    of one block's outputs grows to 4 % of the residual within three blocks,
-    in the oracle itself); two correct implementations then disagree on rows
-    of any margin by the last block."""
+    Depth 1 is strict: every row's argmax equals the oracle's and the logits
+    agree to the MLP tolerance.  With random N(0, 0.02) weights every block's
+    output is as large as the residual stream and fp8 quantization is
+    discontinuous, so deeper blocks amplify any rounding difference; two
+    correct implementations drift apart.  The stored spread (written by the
+    oracle alone, tests/golden/make_stack_expected.py) is the oracle rerun
+    with seeded one-bf16-ulp changes planted in block outputs.  At every
+    depth 1..24 the GPU must lie inside it: argmax agreement at least the
+    lowest of the perturbed runs, relative logit error at most their largest,
+    and no more mismatching rows outside the near-tie band than the worst of
+    them."""
     d = dev()
     note("decode stack 24 x (d=2560 ffn=9728 block) M=64 + bf16 head 4096x2560")
     _cache.clear()
     exp = np.load(STACK_EXPECTED)
+    fams = [k[:-len("_agree")] for k in exp.files if k.endswith("_agree")]
+    spread = {s: np.concatenate([exp[f"{f}_{s}"] for f in fams]) for s in ("agree", "relerr", "nonneartie")}
     wl = synth.WORKLOADS["stack"]
     M = wl.ms[0]
     head = synth.stack_head(wl).to(d)
@@ -101,29 +129,42 @@ def test_decode_stack_argmax():
     xb = torch.empty((M, wl.d), dtype=torch.bfloat16, device=d)
     y = torch.empty((M, wl.d), dtype=torch.bfloat16, device=d)
     ws = sgd.Workspace(d, sgd.mlp_workspace_bytes("block", M, wl.d, wl.ffn))
-    agree = [int((sgd.argmax_rows(sgd.head_logits(h, head)).cpu().numpy() == exp["argmax"][0]).sum())]
+    stats = [_stack_depth_stats(sgd.head_logits(h, head).cpu().numpy(), exp, 0)]
     for layer in range(wl.layers):
         pws = [sgd.quantize_pack_weight(w.to(d), "block") for w in synth.stack_layer_weights(wl, layer)]
         sgd.rmsnorm_bf16(h, out=xb)
         sgd.fused_swiglu_mlp(xb, *pws, out=y, workspace=ws)
         sgd.residual_add(h, y)
-        lg = sgd.head_logits(h, head)
-        am = sgd.argmax_rows(lg).cpu().numpy()
-        agree.append(int((am == exp["argmax"][layer + 1]).sum()))
+        lg = sgd.head_logits(h, head).cpu().numpy()
+        stats.append(_stack_depth_stats(lg, exp, layer + 1))
         if layer == 0:
-            lg1 = lg.cpu().numpy().astype(np.float64)
-            bad = np.nonzero(am != exp["argmax"][1])[0]
-            ref1 = exp["logits_d1"].astype(np.float64)
-            rf = ref.rel_fro(lg1, ref1)
-            print(f"[parity] stack depth 1: logits rel_fro={rf:.3e} argmax agree {agree[-1]}/{M}", flush=True)
-            assert rf <= ref.REL_FRO_TOL, rf
-            assert bad.size == 0, [(int(r), int(am[r]), int(exp["argmax"][1][r]), float(exp["margin"][1][r]))
-                                   for r in bad]
+            rf1 = ref.rel_fro(lg.astype(np.float64), exp["logits_d1"].astype(np.float64))
         del pws
     torch.cuda.synchronize()
-    lgf = lg.cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(lgf))
-    ref_lg = exp["logits"].astype(np.float64)
-    print(f"[report] stack argmax agreement by depth 0..24 (of {M}): {agree}", flush=True)
-    print(f"[report] stack depth 24: logits rel_fro={ref.rel_fro(lgf, ref_lg):.3e} "
-          f"max|dlogit|={float(np.max(np.abs(lgf - ref_lg))):.3e}", flush=True)
+    assert ws.status() == 0
+    assert np.all(np.isfinite(lg))
+    rf24 = ref.rel_fro(lg.astype(np.float64), exp["logits"].astype(np.float64))
+    print(f"[report] stack depth 1: logits rel_fro={rf1:.3e}; depth 24 (all columns): rel_fro={rf24:.3e}",
+          flush=True)
+    print("[report] depth  agree (spread min)  relerr (spread max)  non-near-tie mismatches (spread max)",
+          flush=True)
+    for dep, st in enumerate(stats):
+        print(f"[report] {dep:5d}  {st['agree']:5d} ({int(spread['agree'][:, dep].min()):3d})"
+              f"  {st['relerr']:.3e} ({spread['relerr'][:, dep].max():.3e})"
+              f"  {st['nonnear']:3d} ({int(spread['nonneartie'][:, dep].max())})", flush=True)
+    # depth 0: the same bf16 input on both sides; any mismatch must be a near-tie
+    assert stats[0]["nonnear"] == 0, stats[0]["bad"]
+    # depth 1: strict
+    assert rf1 <= ref.REL_FRO_TOL, rf1
+    assert stats[1]["agree"] == M, stats[1]["bad"]
+    for dep in range(1, wl.layers + 1):
+        st = stats[dep]
+        assert st["agree"] >= spread["agree"][:, dep].min(), (dep, st["agree"], st["bad"])
+        assert st["relerr"] <= spread["relerr"][:, dep].max(), (dep, st["relerr"])
+        assert st["nonnear"] <= spread["nonneartie"][:, dep].max(), (dep, st["nonnear"], st["bad"])
+    # over all depths: the GPU's mean agreement is not below the worst run's
+    mean_gpu = np.mean([st["agree"] for st in stats[1:]])
+    mean_runs = spread["agree"][:, 1:].mean(axis=1)
+    print(f"[report] mean agreement over depths 1..24: GPU {mean_gpu:.2f}, perturbed runs "
+          f"{mean_runs.min():.2f}..{mean_runs.max():.2f}", flush=True)
+    assert mean_gpu >= mean_runs.min(), (mean_gpu, mean_runs.min())
