@@ -235,6 +235,56 @@ int sgd_fused_swiglu_mlp(const uint16_t* x_bf16, int M, const sgd_weight* gate,
                          uint16_t* y_bf16, void* workspace, size_t ws_bytes,
                          void* stream);
 
+/* ---- the unfused pipeline (three launches, intermediates in HBM) -------- */
+/*
+ * The same MLP as sgd_fused_swiglu_mlp in three launches whose intermediates
+ * go through HBM, the launch-per-step form the fused kernel replaces (Fish
+ * Audio X post, section "Custom kernels for the shapes TTS actually uses":
+ * separate launches for activation, gate multiplication and down projection,
+ * each writing to and reading from HBM; fish.audio blog, section "Resultados
+ * de benchmark del kernel", fusing the SwiGLU prologue into the down GEMM's
+ * activation quantization):
+ *   1. gu [M, 2*ffn] fp32 = Q(x) [Wg; Wu]^T          sgd_scaled_gemm_f32
+ *      (one packed weight [2*ffn, d]: the packed gate followed by the packed
+ *      up, codes after codes and scales after scales, is the packing of the
+ *      stacked matrix, since both layouts run band by band);
+ *   2. Q(a), a = silu(g) * u                         sgd_swiglu_quantize
+ *   3. y = Q(a) Wd^T                                 sgd_scaled_gemm_q
+ *
+ * Activations in the WORKSPACE LAYOUT (the layout sgd_mlp_workspace_layout
+ * documents): codes M*K bytes stored m-tile by m-tile; scales of
+ * sgd_act_scales_bytes bytes (BLOCK128: fp32 [K/128][Mpad], Mpad = M
+ * rounded up to 16, 32, 64 or 128, padded rows zero; MX32: per m-tile and
+ * 128-column k-tile one dword of four E8M0 bytes per row).
+ */
+
+/* y [M, N] fp32 = Q(x) W^T: sgd_scaled_gemm with an fp32 output (16-byte
+ * aligned).  Same workspace and errors. */
+int sgd_scaled_gemm_f32(const uint16_t* x_bf16, int M, const sgd_weight* w,
+                        float* y_f32, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/* Bytes of the scales of M x K activations in the workspace layout; 0 when
+ * invalid (1 <= M <= SGD_MAX_M, K a positive multiple of 128). */
+size_t sgd_act_scales_bytes(int fmt, int M, int K);
+
+/* From gu [M, 2*ffn] fp32 (g in columns [0, ffn), u in [ffn, 2*ffn)):
+ * a = silu(g) * u in fp32, quantized per row along ffn in `fmt` (the rules
+ * of sgd_quantize_act) into codes aq [M*ffn] and scales `as`, workspace
+ * layout.  One launch.  1 <= M <= SGD_MAX_M; ffn a multiple of 128.  gu
+ * and aq 16-byte aligned, as 4-byte aligned.  Errors: SGD_EFMT, SGD_EINVAL,
+ * SGD_EDIM, SGD_EALIGN. */
+int sgd_swiglu_quantize(int fmt, const float* gu, int M, int ffn, uint8_t* aq,
+                        void* as, void* stream);
+
+/* y [M, N] bf16 = Q(x) W^T with Q(x) given already quantized in W's format
+ * (codes xq [M*K] and scales xs in the workspace layout), fp32 accumulation.
+ * Same workspace (sgd_gemm_workspace_bytes) and errors as sgd_scaled_gemm;
+ * xq 16-byte aligned, xs 4-byte aligned. */
+int sgd_scaled_gemm_q(const uint8_t* xq, const void* xs, int M,
+                      const sgd_weight* w, uint16_t* y_bf16, void* workspace,
+                      size_t ws_bytes, void* stream);
+
 /* ---- decode-stack glue (pre-RMSNorm residual blocks + output head) ----- */
 /* h [M, d] fp32 <- x [M, d] bf16 (exact widening).  d multiple of 128. */
 int sgd_bf16_to_f32(const uint16_t* x_bf16, int M, int d, float* h, void* stream);

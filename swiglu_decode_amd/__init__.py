@@ -20,7 +20,8 @@ __all__ = [
     "fmt_code", "quantize_pack_weight", "unpack_weight", "quantize_act", "scaled_gemm",
     "fused_swiglu_mlp", "bf16_to_f32", "rmsnorm_bf16", "residual_add", "head_logits",
     "argmax_rows", "gemm_workspace_bytes", "mlp_workspace_bytes", "lib",
-    "workspace_status", "set_wait_budget_us",
+    "workspace_status", "set_wait_budget_us", "mlp_workspace_layout",
+    "scaled_gemm_f32", "swiglu_quantize", "scaled_gemm_q", "stack_packed", "unfused_swiglu_mlp",
 ]
 
 _FMTS = {"block": FMT_BLOCK128, "mx": FMT_MX32, FMT_BLOCK128: FMT_BLOCK128, FMT_MX32: FMT_MX32}
@@ -278,6 +279,100 @@ def fused_swiglu_mlp(x, gate, up, down, out=None, workspace=None):
             _ptr(ws), ws.numel(), _stream(x)))
     _serialise_persistent(x.device, launch)
     return out
+
+
+def scaled_gemm_f32(x, w, out=None, workspace=None):
+    """y [M, N] fp32 = Q(x) W^T (scaled_gemm with an fp32 output)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    _need(x, "x", torch.bfloat16, device=w.device)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, weight has K={w.K}")
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (M, w.N), x.device)
+    need = lib().sgd_gemm_workspace_bytes(w.fmt, M, w.N, w.K)
+    if need == 0:
+        raise ValueError(f"unsupported GEMM shape M={M} N={w.N} K={w.K}")
+    st = w.c_struct()
+
+    def launch():
+        ws = _workspace(x.device, need, workspace)
+        _lib.check("sgd_scaled_gemm_f32", lib().sgd_scaled_gemm_f32(
+            _ptr(x), M, ctypes.byref(st), _ptr(out), _ptr(ws), ws.numel(), _stream(x)))
+    _serialise_persistent(x.device, launch)
+    return out
+
+
+def swiglu_quantize(gu, fmt, out=None):
+    """From gu [M, 2*ffn] fp32 (gate columns first, then up): Q(silu(g) * u)
+    as (codes uint8 [M*ffn], scales uint8 [sgd_act_scales_bytes]) in the
+    workspace layout (see swiglu_decode.h)."""
+    f = fmt_code(fmt)
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be [M, 2*ffn]")
+    _need(gu, "gu", torch.float32)
+    M, F = gu.shape[0], gu.shape[1] // 2
+    nsc = lib().sgd_act_scales_bytes(f, M, F)
+    if nsc == 0:
+        raise ValueError(f"unsupported shape M={M} ffn={F}")
+    if out is None:
+        out = (torch.empty(M * F, dtype=torch.uint8, device=gu.device),
+               torch.empty(nsc, dtype=torch.uint8, device=gu.device))
+    aq, sc = out
+    _need(aq, "codes", torch.uint8, (M * F,), gu.device)
+    _need(sc, "scales", torch.uint8, (nsc,), gu.device)
+    _lib.check("sgd_swiglu_quantize",
+               lib().sgd_swiglu_quantize(f, _ptr(gu), M, F, _ptr(aq), _ptr(sc), _stream(gu)))
+    return aq, sc
+
+
+def scaled_gemm_q(xq, xs, M, w, out=None, workspace=None):
+    """y [M, N] bf16 = Q(x) W^T from activations already quantized in the
+    workspace layout (codes xq uint8 [M*K], scales xs uint8)."""
+    _need(xq, "xq", torch.uint8, (M * w.K,), w.device)
+    _need(xs, "xs", torch.uint8, (lib().sgd_act_scales_bytes(w.fmt, M, w.K),), w.device)
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=xq.device)
+    _need(out, "out", torch.bfloat16, (M, w.N), xq.device)
+    need = lib().sgd_gemm_workspace_bytes(w.fmt, M, w.N, w.K)
+    if need == 0:
+        raise ValueError(f"unsupported GEMM shape M={M} N={w.N} K={w.K}")
+    st = w.c_struct()
+
+    def launch():
+        ws = _workspace(xq.device, need, workspace)
+        _lib.check("sgd_scaled_gemm_q", lib().sgd_scaled_gemm_q(
+            _ptr(xq), _ptr(xs), M, ctypes.byref(st), _ptr(out), _ptr(ws), ws.numel(), _stream(xq)))
+    _serialise_persistent(xq.device, launch)
+    return out
+
+
+def stack_packed(a, b):
+    """The packed weight of the row-stacked matrix [A; B] from packed A and B
+    of one format and width (both packed layouts run band by band, so this is
+    a concatenation of their codes and of their scales)."""
+    if a.fmt != b.fmt or a.K != b.K or a.device != b.device:
+        raise ValueError("weights to stack must share format, K and device")
+    return PackedWeight(a.fmt, a.N + b.N, a.K, torch.cat([a.codes, b.codes]), torch.cat([a.scales, b.scales]))
+
+
+def unfused_swiglu_mlp(x, gate_up, down, out=None, workspace=None, buffers=None):
+    """The SwiGLU MLP in three launches with HBM intermediates: the gate/up
+    GEMM into fp32 gu [M, 2*ffn] (gate_up = stack_packed(gate, up)), the
+    standalone SwiGLU + re-quantization, the down GEMM from Q(a).  `buffers`
+    (gu, aq, as) may be passed to reuse them (e.g. under graph capture)."""
+    M = x.shape[0]
+    F = gate_up.N // 2
+    if buffers is None:
+        buffers = (torch.empty((M, 2 * F), dtype=torch.float32, device=x.device),
+                   torch.empty(M * F, dtype=torch.uint8, device=x.device),
+                   torch.empty(lib().sgd_act_scales_bytes(gate_up.fmt, M, F), dtype=torch.uint8, device=x.device))
+    gu, aq, sc = buffers
+    scaled_gemm_f32(x, gate_up, out=gu, workspace=workspace)
+    swiglu_quantize(gu, gate_up.fmt, out=(aq, sc))
+    return scaled_gemm_q(aq, sc, M, down, out=out, workspace=workspace)
 
 
 def bf16_to_f32(x, out=None):

@@ -48,6 +48,10 @@ SIGNATURES = {
     "sgd_workspace_clear": (_i, [_vp, _sz, _vp]),
     "sgd_scaled_gemm": (_i, [_vp, _i, _wp, _vp, _vp, _sz, _vp]),
     "sgd_fused_swiglu_mlp": (_i, [_vp, _i, _wp, _wp, _wp, _vp, _vp, _sz, _vp]),
+    "sgd_scaled_gemm_f32": (_i, [_vp, _i, _wp, _vp, _vp, _sz, _vp]),
+    "sgd_act_scales_bytes": (_sz, [_i, _i, _i]),
+    "sgd_swiglu_quantize": (_i, [_i, _vp, _i, _i, _vp, _vp, _vp]),
+    "sgd_scaled_gemm_q": (_i, [_vp, _vp, _i, _wp, _vp, _vp, _sz, _vp]),
     "sgd_bf16_to_f32": (_i, [_vp, _i, _i, _vp, _vp]),
     "sgd_rmsnorm_bf16": (_i, [_vp, _i, _i, _f, _vp, _vp]),
     "sgd_residual_add": (_i, [_vp, _vp, _i, _i, _vp]),

@@ -49,6 +49,19 @@ int check_weight(const sgd_weight* w) {
 
 namespace sgd {
 uint64_t wait_budget_ticks() { return (uint64_t)g_wait_budget_us.load(std::memory_order_relaxed) * 100u; }
+
+int check_mlp_args(const uint16_t* x_bf16, int M, const sgd_weight* gate, const sgd_weight* up,
+                   const sgd_weight* down, const uint16_t* y_bf16) {
+  int rc;
+  if ((rc = check_weight(gate)) || (rc = check_weight(up)) || (rc = check_weight(down))) return rc;
+  if (gate->fmt != up->fmt || gate->fmt != down->fmt) return SGD_EFMT;
+  const int d = gate->K, F = gate->N;
+  if (up->N != F || up->K != d || down->N != d || down->K != F) return SGD_EDIM;
+  if (F > 32768) return SGD_EINVAL;
+  if (!x_bf16 || !y_bf16 || M <= 0 || M > SGD_MAX_M) return SGD_EINVAL;
+  if (!al16(x_bf16) || !al16(y_bf16)) return SGD_EALIGN;
+  return SGD_OK;
+}
 }  // namespace sgd
 
 extern "C" {
@@ -181,17 +194,71 @@ int sgd_scaled_gemm(const uint16_t* x_bf16, int M, const sgd_weight* w, uint16_t
   return launch_stream(p, as_stream(stream));
 }
 
+int sgd_scaled_gemm_f32(const uint16_t* x_bf16, int M, const sgd_weight* w, float* y_f32, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (!x_bf16 || !y_f32 || M <= 0 || M > SGD_MAX_M) return SGD_EINVAL;
+  if (!al16(x_bf16) || !al16(y_f32)) return SGD_EALIGN;
+  if (!workspace) return SGD_EWORKSPACE;
+  if (!al16(workspace)) return SGD_EALIGN;
+  const size_t need = stream_workspace_bytes(w->fmt, M, w->K, 0, w->N, w->K, false);
+  if (need == 0) return SGD_EDIM;
+  if (ws_bytes < need) return SGD_EWORKSPACE;
+  Problem p{};
+  p.fmt = w->fmt;
+  p.M = M;
+  p.x = x_bf16;
+  p.K1 = w->K;
+  p.w2 = w;
+  p.y32 = y_f32;
+  p.ws = workspace;
+  return launch_stream(p, as_stream(stream));
+}
+
+size_t sgd_act_scales_bytes(int fmt, int M, int K) {
+  if (!fmt_ok(fmt) || M <= 0 || M > SGD_MAX_M || K <= 0 || K > MAX_DIM || (K % 128)) return 0;
+  return fmt == SGD_FMT_BLOCK128 ? (size_t)(K / 128) * (size_t)act_mtile_pad(M) * 4 : (size_t)M * (size_t)(K / 32);
+}
+
+int sgd_swiglu_quantize(int fmt, const float* gu, int M, int ffn, uint8_t* aq, void* as, void* stream) {
+  if (!fmt_ok(fmt)) return SGD_EFMT;
+  if (!gu || !aq || !as || M <= 0 || M > SGD_MAX_M || ffn <= 0 || ffn > MAX_DIM) return SGD_EINVAL;
+  if (ffn % 128) return SGD_EDIM;
+  if (!al16(gu) || !al16(aq) || !al4(as)) return SGD_EALIGN;
+  return launch_swiglu_quantize(fmt, gu, M, ffn, aq, as, as_stream(stream));
+}
+
+int sgd_scaled_gemm_q(const uint8_t* xq, const void* xs, int M, const sgd_weight* w, uint16_t* y_bf16,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (!xq || !xs || !y_bf16 || M <= 0 || M > SGD_MAX_M) return SGD_EINVAL;
+  if (!al16(xq) || !al4(xs) || !al16(y_bf16)) return SGD_EALIGN;
+  if (!workspace) return SGD_EWORKSPACE;
+  if (!al16(workspace)) return SGD_EALIGN;
+  const size_t need = stream_workspace_bytes(w->fmt, M, w->K, 0, w->N, w->K, false);
+  if (need == 0) return SGD_EDIM;
+  if (ws_bytes < need) return SGD_EWORKSPACE;
+  Problem p{};
+  p.fmt = w->fmt;
+  p.M = M;
+  p.x = nullptr;
+  p.K1 = w->K;
+  p.w2 = w;
+  p.y = y_bf16;
+  p.ws = workspace;
+  p.xq_in = xq;
+  p.xs_in = xs;
+  return launch_stream(p, as_stream(stream));
+}
+
 int sgd_fused_swiglu_mlp(const uint16_t* x_bf16, int M, const sgd_weight* gate, const sgd_weight* up,
                          const sgd_weight* down, uint16_t* y_bf16, void* workspace, size_t ws_bytes,
                          void* stream) {
-  int rc;
-  if ((rc = check_weight(gate)) || (rc = check_weight(up)) || (rc = check_weight(down))) return rc;
-  if (gate->fmt != up->fmt || gate->fmt != down->fmt) return SGD_EFMT;
+  int rc = sgd::check_mlp_args(x_bf16, M, gate, up, down, y_bf16);
+  if (rc) return rc;
   const int d = gate->K, F = gate->N;
-  if (up->N != F || up->K != d || down->N != d || down->K != F) return SGD_EDIM;
-  if (F > 32768) return SGD_EINVAL;
-  if (!x_bf16 || !y_bf16 || M <= 0 || M > SGD_MAX_M) return SGD_EINVAL;
-  if (!al16(x_bf16) || !al16(y_bf16)) return SGD_EALIGN;
   if (!workspace) return SGD_EWORKSPACE;
   if (!al16(workspace)) return SGD_EALIGN;
   const size_t need = stream_workspace_bytes(gate->fmt, M, d, F, d, F, true);

@@ -28,14 +28,27 @@ struct Problem {
   const sgd_weight* gate;
   const sgd_weight* up;
   const sgd_weight* w2;  // down [d, F] (MLP) or W [N, K] (GEMM)
-  uint16_t* y;         // [M, w2->N]
+  uint16_t* y;         // [M, w2->N] bf16
   void* ws;
+  float* y32 = nullptr;               // fp32 output instead of y
+  const uint8_t* xq_in = nullptr;     // x already quantized (workspace layout), x unused
+  const void* xs_in = nullptr;
 };
 size_t stream_workspace_bytes(int fmt, int M, int K1, int F, int N, int K2, bool mlp);
 // Byte offsets of the fused MLP's workspace regions: Q(x) codes, Q(x)
 // scales, a (fp32), Q(a) codes, Q(a) scales.
 int stream_workspace_layout(int fmt, int M, int K1, int F, size_t (&off)[5]);
+// Rows of the activation scale layout (block format): M rounded up to 16,
+// 32, 64 or 128.
+int act_mtile_pad(int M);
+// a = silu(g) * u from gu [M, 2F] fp32, quantized into the workspace layout.
+int launch_swiglu_quantize(int fmt, const float* gu, int M, int F, uint8_t* aq, void* as, hipStream_t s);
 int launch_stream(const Problem& p, hipStream_t s);
+
+// Host-side validation of a fused-MLP call's arguments other than its
+// workspace: SGD_OK or the status the C ABI returns.
+int check_mlp_args(const uint16_t* x_bf16, int M, const sgd_weight* gate, const sgd_weight* up,
+                   const sgd_weight* down, const uint16_t* y_bf16);
 
 // Decode-stack glue.
 int launch_bf16_to_f32(const uint16_t* x, int M, int d, float* h, hipStream_t s);
@@ -44,6 +57,10 @@ int launch_residual_add(float* h, const uint16_t* y, int M, int d, hipStream_t s
 int launch_residual_rmsnorm(float* h, const uint16_t* y, int M, int d, float eps, uint16_t* x, hipStream_t s);
 int launch_head(const float* h, int M, int K, const uint16_t* w, int N, float* out, hipStream_t s);
 int launch_argmax(const float* logits, int M, int N, int32_t* out, hipStream_t s);
+
+// The workspace's leading control block (zeroed once; left ready by every
+// completed call).
+constexpr size_t CONTROL_BLOCK_BYTES = size_t(256) << 10;
 
 // Word of the workspace control block that counts waits that gave up
 // (sticky until the workspace is cleared).

@@ -105,7 +105,8 @@ struct Args {
   const uint8_t* w2;         // second GEMM weight [N, K2]
   const void* s2;
   int N, K2;
-  uint16_t* y;               // [M, N] bf16
+  uint16_t* y;               // [M, N] bf16 (when y32 is null)
+  float* y32;                // [M, N] fp32 output instead, or null
   uint32_t* ctrl;
   uint8_t* xa;               // codes of Q(x) [M, K1]
   void* xs;                  // x scales: block fp32 [K1/128][Mpad]; mx u8 [M][K1/32]
@@ -144,6 +145,7 @@ constexpr int C_GPCNT = C_GCNT + 512;              // arrivals on shared GU band
 constexpr int C_DPCNT = C_GPCNT + 2048;            // arrivals on shared DN bands
 constexpr int CTRL_WORDS = 65536;
 constexpr size_t CTRL_BYTES = (size_t)CTRL_WORDS * 4;
+static_assert(CTRL_BYTES == CONTROL_BLOCK_BYTES, "control block size");
 constexpr int MAX_ITEMS = 512, MAX_GROUPS = 512, MAX_GBANDS = 2048;
 // Workgroups a grid may have; the workspace holds two partial-sum slots for each.
 constexpr int MAX_WG = 512;
@@ -1216,7 +1218,13 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int row = mt * 16 + 4 * (l >> 4) + rr;
-        if (row < a.M) a.y[(size_t)row * a.N + b * 32 + nb * 16 + (l & 15)] = (uint16_t)f32_to_bf16(s[nb][mt][rr]);
+        if (row < a.M) {
+          const size_t o = (size_t)row * a.N + b * 32 + nb * 16 + (l & 15);
+          if (a.y32)
+            a.y32[o] = s[nb][mt][rr];
+          else
+            a.y[o] = (uint16_t)f32_to_bf16(s[nb][mt][rr]);
+        }
       }
 }
 
@@ -1432,6 +1440,56 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
 }
 
 // ---------------------------------------------------------------------------
+// Standalone SwiGLU + re-quantization (the middle launch of the unfused
+// pipeline: gate/up GEMM, this, down GEMM, with the intermediates in HBM).
+// gu [M, 2F] fp32 holds g in columns [0, F) and u in [F, 2F).  One
+// wavefront per (128-column group, 16-row tile), one lane per (row,
+// 32-column block), the arithmetic of the fused kernel's band finish and
+// group re-quantization: a = silu(g) * u in fp32, then quant_block32.  Q(a)
+// is written in the workspace layout (codes m-tile by m-tile; block scales
+// [F/128][Mpad] with padded rows zero; MX scales per m-tile and k-tile).
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ __launch_bounds__(256) void swiglu_quant_kernel(const float* __restrict__ gu, int M, int F, int Mpad,
+                                                           uint8_t* __restrict__ aq, void* __restrict__ as) {
+  const int nmt = (M + 15) >> 4;
+  const int wave = (int)((blockIdx.x * 256u + threadIdx.x) >> 6);
+  if (wave >= (F >> 7) * nmt) return;
+  const int g = wave / nmt, mt = wave - g * nmt;
+  const int l = lane_id(), row = mt * 16 + (l >> 2), j = l & 3;
+  if (row < M) {  // (the 4 lanes of a row agree)
+    const float4* pg = reinterpret_cast<const float4*>(gu + (size_t)row * 2 * F + g * 128 + 32 * j);
+    const float4* pu = reinterpret_cast<const float4*>(gu + (size_t)row * 2 * F + F + g * 128 + 32 * j);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float4 x = pg[c], y = pu[c];
+      v[4 * c] = silu_mul(x.x, y.x);
+      v[4 * c + 1] = silu_mul(x.y, y.y);
+      v[4 * c + 2] = silu_mul(x.z, y.z);
+      v[4 * c + 3] = silu_mul(x.w, y.w);
+    }
+    uint32_t cw[8], se = 0;
+    float sf = 1.0f;
+    quant_block32<FMT>(v, cw, &sf, &se);
+    const uint32_t off = act_code_off(M, F, row, g * 128 + 32 * j);
+    *reinterpret_cast<uint4*>(aq + off) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    *reinterpret_cast<uint4*>(aq + off + 16u * act_tile_rows(M, row)) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+    if (FMT == FMT_BLOCK) {
+      if (j == 0) static_cast<float*>(as)[(size_t)g * Mpad + row] = sf;
+    } else {
+      const uint32_t e4 = pack4_lanes(se);
+      if (j == 0) *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(as) + act_scale_off(M, F, row, g)) = e4;
+    }
+  }
+  if (FMT == FMT_BLOCK && mt == 0) {
+    float* col = static_cast<float*>(as) + (size_t)g * Mpad;
+    if (l >= M && l < Mpad) col[l] = 0.0f;
+    if (l + 64 >= M && l + 64 < Mpad) col[l + 64] = 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side: plan, workspace layout, launch
 // ---------------------------------------------------------------------------
 namespace {
@@ -1622,6 +1680,19 @@ size_t stream_workspace_bytes(int fmt, int M, int K1, int F, int N, int K2, bool
   return p.ok ? p.bytes : 0;
 }
 
+int act_mtile_pad(int M) { return 16 * mt_for(M); }
+
+int launch_swiglu_quantize(int fmt, const float* gu, int M, int F, uint8_t* aq, void* as, hipStream_t s) {
+  const int Mpad = 16 * mt_for(M);
+  const size_t waves = (size_t)(F / 128) * (size_t)((M + 15) / 16);
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (fmt == FMT_BLOCK)
+    hipLaunchKernelGGL(swiglu_quant_kernel<FMT_BLOCK>, grid, dim3(256), 0, s, gu, M, F, Mpad, aq, as);
+  else
+    hipLaunchKernelGGL(swiglu_quant_kernel<FMT_MX>, grid, dim3(256), 0, s, gu, M, F, Mpad, aq, as);
+  return hip_status(hipGetLastError());
+}
+
 int stream_workspace_layout(int fmt, int M, int K1, int F, size_t (&off)[5]) {
   const Plan p = make_plan(fmt, M, K1, F, K1, F, true, MAX_WG);
   if (!p.ok) return SGD_EDIM;
@@ -1637,7 +1708,8 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   const bool mlp = pr.gate != nullptr;
   const int F = mlp ? pr.gate->N : 0;
   const int MT = mt_for(pr.M);
-  const int XL = use_xl(pr.fmt, MT, pr.K1) ? 1 : 0;
+  // (activations given already quantized are read from the caller's buffers)
+  const int XL = !pr.xq_in && use_xl(pr.fmt, MT, pr.K1) ? 1 : 0;
   int G = 0;
   int rc = grid_size(MT, pr.fmt, XL, mlp, &G);
   if (rc != SGD_OK) return rc;
@@ -1664,6 +1736,7 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.K2 = pr.w2->K;
   a.scale_bytes_2 = (uint32_t)sgd_packed_scales_bytes(pr.fmt, a.N, a.K2);
   a.y = pr.y;
+  a.y32 = pr.y32;
   uint8_t* ws = static_cast<uint8_t*>(pr.ws);
   a.ctrl = reinterpret_cast<uint32_t*>(ws);
   a.xa = ws + p.off_xa;
@@ -1676,6 +1749,12 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.G = G;
   a.n_pairs = p.n_pairs;
   a.n_items = XL ? 0 : p.n_items;
+  if (pr.xq_in) {
+    // nothing to quantize: Q(x) is the caller's, in the workspace layout
+    a.xa = const_cast<uint8_t*>(pr.xq_in);
+    a.xs = const_cast<void*>(pr.xs_in);
+    a.n_items = 0;
+  }
   a.ngroups = p.ngroups;
   a.ks = p.ks;
   a.budget = wait_budget_ticks();
