@@ -235,6 +235,30 @@ int sgd_fused_swiglu_mlp(const uint16_t* x_bf16, int M, const sgd_weight* gate,
                          uint16_t* y_bf16, void* workspace, size_t ws_bytes,
                          void* stream);
 
+/*
+ * The fused SwiGLU MLP for callers that cannot allocate device memory (code
+ * under graph capture that may not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation): the same computation and kernel as
+ * sgd_fused_swiglu_mlp, with the workspace taken from a fixed array of
+ * SGD_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends (device-side static memory; no hipMalloc,
+ * hipFree or allocating library call is made).  The caller passes inputs and
+ * outputs as for sgd_fused_swiglu_mlp.  Shapes whose workspace
+ * (sgd_mlp_workspace_bytes) exceeds the array return SGD_EWORKSPACE; every
+ * M <= 128 with d <= 16384 and ffn <= 32768 fits.  The first call on a device
+ * zero-fills the array's control block with a kernel on `stream`.  All calls
+ * on one GPU share its array and it keeps the last call's contents: calls
+ * that overlap on one GPU (two streams, two threads) race and must be
+ * serialised by the caller, also against each other's graph replays.  A
+ * wait that gives up (see the wait budget) leaves that call's output
+ * invalid with no status to query; use the workspace entry point where that
+ * matters.  Errors as sgd_fused_swiglu_mlp.
+ */
+#define SGD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sgd_fused_swiglu_mlp_noalloc(const uint16_t* x_bf16, int M, const sgd_weight* gate,
+                                 const sgd_weight* up, const sgd_weight* down,
+                                 uint16_t* y_bf16, void* stream);
+
 /* ---- the unfused pipeline (three launches, intermediates in HBM) -------- */
 /*
  * The same MLP as sgd_fused_swiglu_mlp in three launches whose intermediates

@@ -20,7 +20,7 @@ __all__ = [
     "fmt_code", "quantize_pack_weight", "unpack_weight", "quantize_act", "scaled_gemm",
     "fused_swiglu_mlp", "bf16_to_f32", "rmsnorm_bf16", "residual_add", "head_logits",
     "argmax_rows", "gemm_workspace_bytes", "mlp_workspace_bytes", "lib",
-    "workspace_status", "set_wait_budget_us", "mlp_workspace_layout",
+    "workspace_status", "set_wait_budget_us", "mlp_workspace_layout", "fused_swiglu_mlp_noalloc",
     "scaled_gemm_f32", "swiglu_quantize", "scaled_gemm_q", "stack_packed", "unfused_swiglu_mlp",
 ]
 
@@ -373,6 +373,22 @@ def unfused_swiglu_mlp(x, gate_up, down, out=None, workspace=None, buffers=None)
     scaled_gemm_f32(x, gate_up, out=gu, workspace=workspace)
     swiglu_quantize(gu, gate_up.fmt, out=(aq, sc))
     return scaled_gemm_q(aq, sc, M, down, out=out, workspace=workspace)
+
+
+def fused_swiglu_mlp_noalloc(x, gate, up, down, out):
+    """The fused MLP through the entry point that allocates nothing (its
+    workspace is the library's fixed per-device array): y [M, d] bf16 into
+    the caller's `out`."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, d]")
+    _need(x, "x", torch.bfloat16, device=gate.device)
+    M, d = x.shape
+    _need(out, "out", torch.bfloat16, (M, d), x.device)
+    g, u, dn = gate.c_struct(), up.c_struct(), down.c_struct()
+    _serialise_persistent(x.device, lambda: _lib.check(
+        "sgd_fused_swiglu_mlp_noalloc", lib().sgd_fused_swiglu_mlp_noalloc(
+            _ptr(x), M, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), _ptr(out), _stream(x))))
+    return out
 
 
 def bf16_to_f32(x, out=None):

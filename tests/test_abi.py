@@ -114,6 +114,17 @@ def test_argument_errors_launch_nothing(L):
     assert args(g, u, d, need - 16) == E["EWORKSPACE"]
     gb, ub, db = _w(N=1 << 15, K=1 << 16), _w(N=1 << 15, K=1 << 16), _w(N=1 << 16, K=1 << 15)
     assert args(gb, ub, db, 1 << 40) == E["EDIM"]
+    # the entry point without a workspace: same argument checks, and shapes
+    # whose workspace exceeds its fixed array are refused before any launch
+    na = lambda g_, u_, d_, M=4, x=0x1000: L.sgd_fused_swiglu_mlp_noalloc(
+        P(x), M, ctypes.byref(g_), ctypes.byref(u_), ctypes.byref(d_), P(0x1000), None)
+    assert na(g, u, _w(N=256, K=384)) == E["EDIM"]
+    assert na(g, u, d, M=0) == E["EINVAL"]
+    assert na(g, u, d, x=0x1002) == E["EALIGN"]
+    assert na(g, _w(fmt=MX, N=512, K=256), d) == E["EFMT"]
+    wide_g, wide_u, wide_d = _w(N=128, K=262144), _w(N=128, K=262144), _w(N=262144, K=128)
+    assert L.sgd_mlp_workspace_bytes(BLK, 128, 262144, 128) > (64 << 20)
+    assert na(wide_g, wide_u, wide_d, M=128) == E["EWORKSPACE"]
     # workspace status query: argument errors only (no GPU here)
     assert L.sgd_workspace_status(None, None) == E["EINVAL"]
     assert L.sgd_workspace_status(P(0x1004), None) == E["EALIGN"]
