@@ -225,41 +225,58 @@ def bench_m(torch, sgd, st, dev, stream, M, steps, warmup, eager_n, unfused=True
 
 
 def bench_stack(torch, sgd, dev, steps, warmup):
-    """The decode step of the 24-block stack: h = f32(x); per block
-    x_l = bf16(RMSNorm(h)), y_l = fused MLP(x_l), h += y_l (the add and the
-    next block's RMSNorm in one launch); then the bf16 head and the argmax of
-    every row.  All 24 packed layers stay resident (1.8 GB, far beyond the
-    Infinity Cache, so each step reads them cold); the step is captured once
-    as a hipGraph and replayed, timed with HIP events on its stream.  The 24
-    fused MLP launches alone are timed the same way (per-layer figure).
-    Algorithmic bytes per step = per block (fp8 weights + scales + bf16 x_l +
-    bf16 y_l) + bf16 head + f32 logits."""
+    """The decode step of the 24-block stack: h = f32(x); 24 blocks, each ONE
+    launch (sgd_fused_swiglu_block: RMSNorm prologue, fused MLP, residual
+    epilogue, h alternating between two fp32 buffers); then the bf16 head and
+    the argmax of every row.  All 24 packed layers stay resident (1.8 GB, far
+    beyond the Infinity Cache, so each step reads them cold); the step is
+    captured once as a hipGraph and replayed, timed with HIP events on its
+    stream.  The 24 block launches alone are timed the same way (per-block
+    figure), and so is the same step built from separate launches (RMSNorm,
+    fused MLP, and the residual add fused with the next RMSNorm), for
+    comparison.  Algorithmic bytes per step = per block (fp8 weights + scales
+    + fp32 h in + fp32 h out) + bf16 head + f32 logits."""
     import synth
+    eps = 1e-6  # RMSNorm epsilon of the stack
     wl = synth.WORKLOADS["stack"]
     M, d, F = wl.ms[0], wl.d, wl.ffn
     layers = [[sgd.quantize_pack_weight(w.to(dev), "block") for w in synth.stack_layer_weights(wl, layer)]
               for layer in range(wl.layers)]
     head = synth.stack_head(wl).to(dev)
     x = synth.stack_x(wl, M).to(dev)
-    h = torch.empty((M, d), dtype=torch.float32, device=dev)
+    ha = torch.empty((M, d), dtype=torch.float32, device=dev)
+    hb = torch.empty((M, d), dtype=torch.float32, device=dev)
     xb = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
     y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
     lg = torch.empty((M, wl.vocab), dtype=torch.float32, device=dev)
     tok = torch.empty((M,), dtype=torch.int32, device=dev)
     ws = sgd.Workspace(dev, sgd.mlp_workspace_bytes("block", M, d, F))
-    layer_bytes = sum(int(p.codes.numel()) + int(p.scales.numel()) for p in layers[0]) + 2 * M * d * 2
+    layer_bytes = sum(int(p.codes.numel()) + int(p.scales.numel()) for p in layers[0]) + 2 * M * d * 4
     step_bytes = wl.layers * layer_bytes + int(head.numel()) * 2 + M * wl.vocab * 4
 
+    def blocks():
+        cur, nxt = ha, hb
+        for pws in layers:
+            sgd.fused_swiglu_block(cur, *pws, eps=eps, out=nxt, workspace=ws)
+            cur, nxt = nxt, cur
+        return cur
+
     def step():
-        sgd.bf16_to_f32(x, out=h)
-        sgd.rmsnorm_bf16(h, out=xb)
+        sgd.bf16_to_f32(x, out=ha)
+        h = blocks()
+        sgd.head_logits(h, head, out=lg)
+        sgd.argmax_rows(lg, out=tok)
+
+    def step_separate():
+        sgd.bf16_to_f32(x, out=ha)
+        sgd.rmsnorm_bf16(ha, eps, out=xb)
         for i, pws in enumerate(layers):
             sgd.fused_swiglu_mlp(xb, *pws, out=y, workspace=ws)
             if i + 1 < len(layers):
-                sgd.residual_rmsnorm_bf16(h, y, out=xb)
+                sgd.residual_rmsnorm_bf16(ha, y, eps, out=xb)
             else:
-                sgd.residual_add(h, y)
-        sgd.head_logits(h, head, out=lg)
+                sgd.residual_add(ha, y)
+        sgd.head_logits(ha, head, out=lg)
         sgd.argmax_rows(lg, out=tok)
 
     stream = torch.cuda.Stream()
@@ -267,20 +284,33 @@ def bench_stack(torch, sgd, dev, steps, warmup):
         step()
         stream.synchronize()
         tok_eager = tok.clone()
+        lg_eager = lg.clone()
         g = capture(torch, stream, [step])
         reps = time_replays(torch, stream, g, steps, warmup, 1)
-        gl = capture(torch, stream, [lambda p=p: sgd.fused_swiglu_mlp(xb, *p, out=y, workspace=ws) for p in layers])
+        graph_equal = bool(torch.equal(tok, tok_eager)) and bool(torch.equal(lg, lg_eager))
+        del g
+        gl = capture(torch, stream, [blocks])
         lreps = time_replays(torch, stream, gl, steps, 2, wl.layers)
+        del gl
+        step_separate()
+        stream.synchronize()
+        separate_equal = bool(torch.equal(lg, lg_eager))
+        gs = capture(torch, stream, [step_separate])
+        sreps = time_replays(torch, stream, gs, max(5, steps // 2), 2, 1)
+        del gs
     us = sum(reps) / len(reps)
     lus = sum(lreps) / len(lreps)
-    out = dict(workload=f"{wl.layers} x (RMSNorm, fused SwiGLU MLP d={d} ffn={F} 128x128 block fp8, residual add) "
-                        f"+ bf16 head {wl.vocab}x{d} + argmax, M={M}, one hipGraph",
+    sus = sum(sreps) / len(sreps)
+    out = dict(workload=f"{wl.layers} x (RMSNorm, fused SwiGLU MLP d={d} ffn={F} 128x128 block fp8, residual add: "
+                        f"one launch per block) + bf16 head {wl.vocab}x{d} + argmax, M={M}, one hipGraph",
                us_per_step=round(us, 2), step_p10_p50_p90=[pct(reps, 10), pct(reps, 50), pct(reps, 90)],
                us_per_block=round(us / wl.layers, 2), algorithmic_bytes_per_step=step_bytes,
                gbs=round(step_bytes / us / 1e3, 1), pct_of_peak=round(100.0 * step_bytes / us / 1e3 / HBM_PEAK_GBS, 1),
-               fused_mlp_us_per_layer=round(lus, 2),
-               fused_mlp_layer_pct_of_peak=round(100.0 * layer_bytes / lus / 1e3 / HBM_PEAK_GBS, 1),
-               graph_tokens_equal_eager=bool(torch.equal(tok, tok_eager)))
+               fused_block_us_per_layer=round(lus, 2),
+               fused_block_layer_pct_of_peak=round(100.0 * layer_bytes / lus / 1e3 / HBM_PEAK_GBS, 1),
+               separate_launches_us_per_step=round(sus, 2),
+               separate_launches_logits_equal=separate_equal,
+               graph_tokens_equal_eager=graph_equal)
     del layers
     torch.cuda.empty_cache()
     return out

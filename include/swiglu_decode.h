@@ -259,6 +259,28 @@ int sgd_fused_swiglu_mlp_noalloc(const uint16_t* x_bf16, int M, const sgd_weight
                                  const sgd_weight* up, const sgd_weight* down,
                                  uint16_t* y_bf16, void* stream);
 
+/*
+ * One pre-RMSNorm residual decode block in ONE launch: the fused SwiGLU MLP
+ * with its RMSNorm prologue and residual epilogue,
+ *   h_out = fl32( h_in + bf16( MLP( bf16( h_in / sqrt(mean(h_in^2) + eps) ) ) ) )
+ * per row (unit-gain RMSNorm, Zhang & Sennrich 2019; MLP as
+ * sgd_fused_swiglu_mlp).  The kernel forms x = bf16(RMSNorm(h_in)) itself,
+ * bit-identical to sgd_rmsnorm_bf16, and adds the bf16 MLP output to h_in in
+ * fp32 as sgd_residual_add does, so the result is bit-identical to
+ * sgd_rmsnorm_bf16 + sgd_fused_swiglu_mlp + sgd_residual_add.  A decode step
+ * of L blocks is then L launches (plus the head), which a caller captures as
+ * one graph: the serving context of the fish.audio blog, sections "Qué hay en
+ * código abierto" (graph-capture safety) and "Hardware y adquisición" (decode
+ * batches up to 64 under graph capture).
+ * h_in, h_out [M, d] fp32, 16-byte aligned; h_out must not overlap h_in
+ * (SGD_EINVAL), so a stack alternates two buffers.  0 <= eps <= 1.  Weights,
+ * workspace (sgd_mlp_workspace_bytes) and errors as sgd_fused_swiglu_mlp.
+ */
+int sgd_fused_swiglu_block(const float* h_in, int M, const sgd_weight* gate,
+                           const sgd_weight* up, const sgd_weight* down, float eps,
+                           float* h_out, void* workspace, size_t ws_bytes,
+                           void* stream);
+
 /* ---- the unfused pipeline (three launches, intermediates in HBM) -------- */
 /*
  * The same MLP as sgd_fused_swiglu_mlp in three launches whose intermediates

@@ -281,6 +281,33 @@ def fused_swiglu_mlp(x, gate, up, down, out=None, workspace=None):
     return out
 
 
+def fused_swiglu_block(h, gate, up, down, eps=1e-6, out=None, workspace=None):
+    """One pre-RMSNorm residual decode block in one launch:
+    h_out [M, d] fp32 = h + bf16(MLP(bf16(RMSNorm(h)))), h [M, d] fp32.
+    `out` must not overlap `h`."""
+    if h.dim() != 2:
+        raise ValueError("h must be 2-D [M, d]")
+    _need(h, "h", torch.float32, device=gate.device)
+    M, d = h.shape
+    if gate.K != d:
+        raise ValueError(f"h has d={d}, gate weight has K={gate.K}")
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.float32, device=h.device)
+    _need(out, "out", torch.float32, (M, d), h.device)
+    need = lib().sgd_mlp_workspace_bytes(gate.fmt, M, d, gate.N)
+    if need == 0:
+        raise ValueError(f"unsupported MLP shape M={M} d={d} ffn={gate.N}")
+    g, u, dn = gate.c_struct(), up.c_struct(), down.c_struct()
+
+    def launch():
+        ws = _workspace(h.device, need, workspace)
+        _lib.check("sgd_fused_swiglu_block", lib().sgd_fused_swiglu_block(
+            _ptr(h), M, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), float(eps), _ptr(out),
+            _ptr(ws), ws.numel(), _stream(h)))
+    _serialise_persistent(h.device, launch)
+    return out
+
+
 def scaled_gemm_f32(x, w, out=None, workspace=None):
     """y [M, N] fp32 = Q(x) W^T (scaled_gemm with an fp32 output)."""
     if x.dim() != 2:

@@ -277,6 +277,39 @@ int sgd_fused_swiglu_mlp(const uint16_t* x_bf16, int M, const sgd_weight* gate, 
   return launch_stream(p, as_stream(stream));
 }
 
+int sgd_fused_swiglu_block(const float* h_in, int M, const sgd_weight* gate, const sgd_weight* up,
+                           const sgd_weight* down, float eps, float* h_out, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  // (the MLP's checks, with h_in and h_out standing in for x and y)
+  int rc = sgd::check_mlp_args(reinterpret_cast<const uint16_t*>(h_in), M, gate, up, down,
+                               reinterpret_cast<const uint16_t*>(h_out));
+  if (rc) return rc;
+  if (!(eps >= 0.0f) || eps > 1.0f) return SGD_EINVAL;
+  const int d = gate->K, F = gate->N;
+  const size_t bytes = (size_t)M * (size_t)d * sizeof(float);
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(h_in), o0 = reinterpret_cast<uintptr_t>(h_out);
+  if (i0 < o0 + bytes && o0 < i0 + bytes) return SGD_EINVAL;  // the output must not overlap the input
+  if (!workspace) return SGD_EWORKSPACE;
+  if (!al16(workspace)) return SGD_EALIGN;
+  const size_t need = stream_workspace_bytes(gate->fmt, M, d, F, d, F, true);
+  if (need == 0) return SGD_EDIM;
+  if (ws_bytes < need) return SGD_EWORKSPACE;
+  Problem p{};
+  p.fmt = gate->fmt;
+  p.M = M;
+  p.x = nullptr;
+  p.K1 = d;
+  p.gate = gate;
+  p.up = up;
+  p.w2 = down;
+  p.y = nullptr;
+  p.ws = workspace;
+  p.h_in = h_in;
+  p.h_out = h_out;
+  p.eps = eps;
+  return launch_stream(p, as_stream(stream));
+}
+
 int sgd_bf16_to_f32(const uint16_t* x_bf16, int M, int d, float* h, void* stream) {
   if (!x_bf16 || !h || M <= 0 || d <= 0 || M > 65536 || d > MAX_DIM) return SGD_EINVAL;
   if (d % 128) return SGD_EDIM;

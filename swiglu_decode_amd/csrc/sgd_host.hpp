@@ -33,6 +33,11 @@ struct Problem {
   float* y32 = nullptr;               // fp32 output instead of y
   const uint8_t* xq_in = nullptr;     // x already quantized (workspace layout), x unused
   const void* xs_in = nullptr;
+  // decode block: x = bf16(RMSNorm(h_in)) formed in the kernel (x unused),
+  // output h_out = fl32(h_in + bf16(y)) (y unused)
+  const float* h_in = nullptr;
+  float* h_out = nullptr;
+  float eps = 0.0f;
 };
 size_t stream_workspace_bytes(int fmt, int M, int K1, int F, int N, int K2, bool mlp);
 // Byte offsets of the fused MLP's workspace regions: Q(x) codes, Q(x)

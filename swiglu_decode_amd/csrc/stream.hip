@@ -105,8 +105,16 @@ struct Args {
   const uint8_t* w2;         // second GEMM weight [N, K2]
   const void* s2;
   int N, K2;
-  uint16_t* y;               // [M, N] bf16 (when y32 is null)
+  uint16_t* y;               // [M, N] bf16 (when y32 and h_out are null)
   float* y32;                // [M, N] fp32 output instead, or null
+  // Decode block (the MLP with its RMSNorm prologue and residual epilogue):
+  // x = bf16(RMSNorm(h_in)) is formed in the kernel and the output is
+  // h_out = fl32(h_in + bf16(y)) instead of y.  Null for the plain MLP.
+  const float* h_in;         // [M, K1] fp32 residual stream
+  float* h_out;              // [M, N] fp32, not overlapping h_in
+  float eps;
+  int row_stash;             // the dynamic LDS holds a row of h_in (K1 floats) for the prologue
+  int row_parts;             // workgroups that share a row's prologue
   uint32_t* ctrl;
   uint8_t* xa;               // codes of Q(x) [M, K1]
   void* xs;                  // x scales: block fp32 [K1/128][Mpad]; mx u8 [M][K1/32]
@@ -945,6 +953,95 @@ __device__ __forceinline__ void xq_item(const Args& a, int item) {
   }
 }
 
+// The decode block's RMSNorm prologue for one row: x = bf16(h / sqrt(mean(h^2)
+// + eps)) (unit gain), quantized into the workspace as xq_item does, by one
+// wavefront: part `part` of `parts` of the row's 128-column groups (each
+// part forms the row's whole sum of squares itself).  The sum of squares is formed in exactly the order of the
+// standalone RMSNorm kernel (256 partial sums, partial t taking the 16-byte
+// chunks t, t + 256, t + 512, t + 768, then t + 1024, ... in one fma chain;
+// a butterfly over each group of 64 partials; the four group sums added in
+// order), so x is bit-identical to that kernel's output.  Lane l holds
+// partials l, 64 + l, 128 + l and 192 + l.  With `stash` (LDS for d floats)
+// the row read for the sum of squares is kept there for the quantization
+// pass, instead of being read from memory again.
+template <int FMT>
+__device__ __forceinline__ void row_prologue(const Args& a, int row, int part, int parts, float* stash) {
+  const int l = lane_id();
+  const int d = a.K1, n4 = d >> 2, ng = d >> 7;
+  const int jb = 4 * ((part * ng) / parts), je = 4 * (((part + 1) * ng) / parts);  // this part's 32-column blocks
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h_in + (size_t)row * d, (uint32_t)d * 4u);
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < n4; c0 += 1024) {
+    v4f v[4][4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 64 * w + l + 256 * u;  // (past the row: zeros, which leave the chain unchanged)
+        v[w][u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rh, c < n4 ? (uint32_t)c * 16u : OOB, 0, 0));
+      }
+    if (stash) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + 64 * w + l + 256 * u;
+          if (c < n4) *reinterpret_cast<v4f*>(stash + 4 * c) = v[w][u];
+        }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss[w] = fmaf(v[w][u][e], v[w][u][e], ss[w]);
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss[w] += __shfl_xor(ss[w], o, WAVE);
+  const float inv = 1.0f / sqrtf((((ss[0] + ss[1]) + ss[2]) + ss[3]) / (float)d + a.eps);
+  // (the stash is written and read by this one wavefront, whose LDS accesses
+  // complete in program order)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const __amdgpu_buffer_rsrc_t rxa = make_rsrc(a.xa, (uint32_t)a.M * (uint32_t)a.K1);
+  // one lane per 32-column block (jb and je are multiples of 4: the four
+  // lanes of a 128-column group agree on j < je)
+  for (int j0 = jb; j0 < je; j0 += 64) {
+    const int j = j0 + l;
+    if (j < je) {
+      float v[32];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const v4f t = stash ? *reinterpret_cast<const v4f*>(stash + 4 * (8 * j + c))
+                            : __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rh, (uint32_t)(8 * j + c) * 16u, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * c + e] = bf16_to_f32(f32_to_bf16(t[e] * inv));
+      }
+      uint32_t cw[8], se = 0;
+      float sf = 1.0f;
+      quant_block32<FMT>(v, cw, &sf, &se);
+      const uint32_t off = act_code_off(a.M, a.K1, row, 32 * j);
+      st_coherent_b128(rxa, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
+      st_coherent_b128(rxa, off + 16u * act_tile_rows(a.M, row), make_uint4(cw[4], cw[5], cw[6], cw[7]));
+      if (FMT == FMT_BLOCK) {
+        if ((j & 3) == 0) st_coherent(static_cast<float*>(a.xs) + (size_t)(j >> 2) * a.Mpad + row, sf);
+      } else {
+        const uint32_t e4 = pack4_lanes(se);
+        if ((j & 3) == 0)
+          st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.xs) + act_scale_off(a.M, a.K1, row, j >> 2)), e4);
+      }
+    }
+  }
+}
+
+// Block-format scales of the padded rows M..Mpad-1 of every group of Q(x): zero.
+__device__ __forceinline__ void zero_pad_x_scales(const Args& a) {
+  const int pad = a.Mpad - a.M, KT1 = a.K1 >> 7;
+  for (int e = lane_id(); e < KT1 * pad; e += 64)
+    st_coherent(static_cast<float*>(a.xs) + (size_t)(e / pad) * a.Mpad + a.M + e % pad, 0.0f);
+}
+
 // Re-quantize 128-column group g of a = silu(g)*u (fp32, written by other
 // workgroups: read agent-coherently), one lane per (row, 32-column block),
 // U blocks per lane at a time with all their loads issued first (one memory
@@ -1024,8 +1121,9 @@ __device__ __forceinline__ void wait_flags(const Guard& g, const uint32_t* flags
   const int l = lane_id();
   uint64_t t0 = 0;
   for (;;) {
+    // (every flag's load issued before any is compared: one round trip a pass)
     bool ok = true;
-    for (int i = l; i < n; i += 64) ok = ok && load_agent(flags + i) == g.ep;
+    for (int i = l; i < n; i += 64) ok &= load_agent(flags + i) == g.ep;
     const uint32_t err_ep = load_agent(g.ctrl + C_ERR_EP);
     if (__all(ok)) break;
     if (must_stop_global(g, err_ep, t0)) break;
@@ -1043,13 +1141,24 @@ __device__ __forceinline__ void mirror_ready(const Guard& gd, Lds<MT, NS, NSLOT>
   const int l = lane_id();
   const int a0 = g0 & ~31;
   uint64_t t0 = 0;
+  constexpr int NIT = MAX_GROUPS / 64;
   for (;;) {
     bool all = true;
     const uint32_t err_ep = load_agent(gd.ctrl + C_ERR_EP);
-    for (int i0 = a0; i0 < g1; i0 += 64) {
+    // every flag's load issued before any is used: one round trip a pass
+    uint32_t f[NIT];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int i = a0 + 64 * k + l;
+      f[k] = i >= g0 && i < g1 ? load_agent(flags + i) : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int i0 = a0 + 64 * k;
+      if (i0 >= g1) break;
       const int i = i0 + l;
       const bool in = i >= g0 && i < g1;
-      const bool r = in && load_agent(flags + i) == gd.ep;
+      const bool r = in && f[k] == gd.ep;
       const uint64_t bal = __ballot(r);
       all = all && __all(r || !in);
       if (l == 0) {
@@ -1206,6 +1315,20 @@ template <int MT>
 __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2][MT]) {
   const int l = lane_id();
   const Phase& ph = a.dn;
+  // decode block: the residual stream's values of this band, loaded ahead of
+  // the split-K combine's round trips
+  float hv[2][MT][4];
+  if (a.h_out) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = mt * 16 + 4 * (l >> 4) + rr;
+          hv[nb][mt][rr] = row < a.M ? a.h_in[(size_t)row * a.N + b * 32 + nb * 16 + (l & 15)] : 0.0f;
+        }
+  }
   const int nsh = owner_wg(ph, b * ph.CPB + ph.CPB - 1) - owner_wg(ph, b * ph.CPB) + 1;
   if (nsh > 1) {
     if (!arrive_shared<MT>(a, ph, a.dpart, a.ctrl + C_DPCNT, b, s, nsh)) return;
@@ -1220,7 +1343,9 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
         const int row = mt * 16 + 4 * (l >> 4) + rr;
         if (row < a.M) {
           const size_t o = (size_t)row * a.N + b * 32 + nb * 16 + (l & 15);
-          if (a.y32)
+          if (a.h_out)  // residual epilogue: the bf16 output added to the fp32 stream
+            a.h_out[o] = hv[nb][mt][rr] + bf16_to_f32(f32_to_bf16(s[nb][mt][rr]));
+          else if (a.y32)
             a.y32[o] = s[nb][mt][rr];
           else
             a.y[o] = (uint16_t)f32_to_bf16(s[nb][mt][rr]);
@@ -1307,9 +1432,18 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
   const uint32_t ep = launch_epoch(a);
   const Guard gd{&L.abort, a.ctrl, a.budget, ep};
   if (!XL) {
-    // quantize this workgroup's share of x, then wait for everyone's
+    // quantize this workgroup's share of x (decode block: its rows, RMSNorm
+    // first), then wait for everyone's
     if (W < a.n_items) {
-      xq_item<FMT>(a, W);
+      if (a.h_in) {
+        // item i: part i % P of row i / P (M * P items, dealt over n_items workgroups)
+        for (int i = W; i < a.M * a.row_parts; i += a.n_items)
+          row_prologue<FMT>(a, i / a.row_parts, i % a.row_parts, a.row_parts,
+                            a.row_stash ? reinterpret_cast<float*>(stages) : nullptr);
+        if (FMT == FMT_BLOCK && W == 0) zero_pad_x_scales(a);
+      } else {
+        xq_item<FMT>(a, W);
+      }
       drain_memory();
       raise_flag(a.ctrl, PG_XQ, W, ep);
     }
@@ -1660,7 +1794,10 @@ int grid_size(int MT, int fmt, int XL, bool mlp, int* out) {
   if (g_occ.per_cu[dev][fi][vi] == 0) {
     const void* kern = pick_kernel(MT, fmt, XL, mlp);
     const int dyn = XL ? LDS_PER_WG - (int)static_lds(MT) : ks_dyn(MT, mlp);
-    if (dyn > 0 && hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess)
+    // (any variant may be launched with up to all the LDS its static part
+    // leaves: the decode block's row stash)
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WG - (int)static_lds(MT)) !=
+        hipSuccess)
       return SGD_EHIP;
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 64 * cfg_nwave(MT), (size_t)dyn) != hipSuccess ||
@@ -1708,11 +1845,22 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   const bool mlp = pr.gate != nullptr;
   const int F = mlp ? pr.gate->N : 0;
   const int MT = mt_for(pr.M);
-  // (activations given already quantized are read from the caller's buffers)
-  const int XL = !pr.xq_in && use_xl(pr.fmt, MT, pr.K1) ? 1 : 0;
+  // (activations given already quantized are read from the caller's
+  // buffers; the decode block quantizes x into the workspace, row by row)
+  const int plain_xl = !pr.xq_in && use_xl(pr.fmt, MT, pr.K1) ? 1 : 0;
+  const int XL = plain_xl && !pr.h_in ? 1 : 0;
+  // (the decode block runs on the grid of the plain MLP's kernel: the same
+  // split of the work, so the same sums, bit for bit)
   int G = 0;
-  int rc = grid_size(MT, pr.fmt, XL, mlp, &G);
+  int rc = grid_size(MT, pr.fmt, plain_xl, mlp, &G);
   if (rc != SGD_OK) return rc;
+  if (pr.h_in && !plain_xl) {
+    // one workgroup per compute unit, which the row stash always leaves room for
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SGD_EHIP;
+    const int cus = g_occ.cus[dev];
+    if (G > cus) G = cus;
+  }
   if (G > MAX_WG) G = MAX_WG;
   const Plan p = make_plan(pr.fmt, pr.M, pr.K1, F, pr.w2->N, pr.w2->K, mlp, G);
   if (!p.ok) return SGD_EDIM;
@@ -1737,6 +1885,19 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.scale_bytes_2 = (uint32_t)sgd_packed_scales_bytes(pr.fmt, a.N, a.K2);
   a.y = pr.y;
   a.y32 = pr.y32;
+  a.h_in = pr.h_in;
+  a.h_out = pr.h_out;
+  a.eps = pr.eps;
+  size_t dyn = XL ? (size_t)((xl_bytes(pr.fmt, p.Mpad, pr.K1) + 15) & ~15) : (size_t)ks_dyn(p.MT, mlp);
+  if (pr.h_in) {
+    // the prologue's row stash, where it fits beside the static LDS (the
+    // dynamic LDS is otherwise unused until the prologue is done)
+    const size_t row = (size_t)pr.K1 * 4;
+    if (static_lds(p.MT) + (row > dyn ? row : dyn) + 1024 <= (size_t)LDS_PER_WG) {
+      a.row_stash = 1;
+      if (row > dyn) dyn = row;
+    }
+  }
   uint8_t* ws = static_cast<uint8_t*>(pr.ws);
   a.ctrl = reinterpret_cast<uint32_t*>(ws);
   a.xa = ws + p.off_xa;
@@ -1749,6 +1910,16 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.G = G;
   a.n_pairs = p.n_pairs;
   a.n_items = XL ? 0 : p.n_items;
+  if (pr.h_in) {
+    // the prologue's items: rows, each split into row_parts shares of its
+    // 128-column groups (as many as the grid has workgroups for)
+    const int ng = pr.K1 / 128;
+    int parts = G / pr.M;
+    if (parts > ng) parts = ng;
+    if (parts < 1) parts = 1;
+    a.row_parts = parts;
+    a.n_items = pr.M * parts < G ? pr.M * parts : G;
+  }
   if (pr.xq_in) {
     // nothing to quantize: Q(x) is the caller's, in the workspace layout
     a.xa = const_cast<uint8_t*>(pr.xq_in);
@@ -1761,7 +1932,6 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.gu = p.gu;
   a.dn = p.dn;
   void* args[] = {&a};
-  const size_t dyn = XL ? (size_t)((xl_bytes(pr.fmt, p.Mpad, pr.K1) + 15) & ~15) : (size_t)ks_dyn(p.MT, mlp);
   return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt, XL, mlp), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, dyn, s));
 }
 

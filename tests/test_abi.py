@@ -125,6 +125,22 @@ def test_argument_errors_launch_nothing(L):
     wide_g, wide_u, wide_d = _w(N=128, K=262144), _w(N=128, K=262144), _w(N=262144, K=128)
     assert L.sgd_mlp_workspace_bytes(BLK, 128, 262144, 128) > (64 << 20)
     assert na(wide_g, wide_u, wide_d, M=128) == E["EWORKSPACE"]
+    # decode block: the MLP's checks, plus eps and an output that must not
+    # overlap the input (h is 4 x 256 fp32 = 4 KB)
+    blk = lambda g_, u_, d_, hi=0x10000, ho=0x20000, eps=1e-6, ws=need, M=4: L.sgd_fused_swiglu_block(
+        P(hi), M, ctypes.byref(g_), ctypes.byref(u_), ctypes.byref(d_), ctypes.c_float(eps), P(ho), P(0x1000), ws,
+        None)
+    assert blk(g, u, _w(N=256, K=384)) == E["EDIM"]
+    assert blk(g, _w(fmt=MX, N=512, K=256), d) == E["EFMT"]
+    assert blk(g, u, d, M=0) == E["EINVAL"]
+    assert blk(g, u, d, hi=0) == E["EINVAL"]
+    assert blk(g, u, d, ho=0x10008) == E["EALIGN"]
+    assert blk(g, u, d, ho=0x10000) == E["EINVAL"]
+    assert blk(g, u, d, ho=0x10000 + 4096 - 16) == E["EINVAL"]
+    assert blk(g, u, d, hi=0x20000 + 4096 - 16) == E["EINVAL"]
+    assert blk(g, u, d, eps=-1.0) == E["EINVAL"]
+    assert blk(g, u, d, eps=float("nan")) == E["EINVAL"]
+    assert blk(g, u, d, ws=need - 16) == E["EWORKSPACE"]
     # workspace status query: argument errors only (no GPU here)
     assert L.sgd_workspace_status(None, None) == E["EINVAL"]
     assert L.sgd_workspace_status(P(0x1004), None) == E["EALIGN"]
