@@ -235,6 +235,7 @@ struct Lds {
   uint32_t prog[NS];               // staged gate/up: k-tiles each streaming wavefront has used
   uint32_t gu_left;                // streaming wavefronts done with gate/up (band finishing included)
   uint32_t abort;                  // a wait of this workgroup gave up: every other wait ends at once
+  float red[4];                    // decode-block prologue: the four wavefront sums of squares
 };
 
 __device__ __forceinline__ uint32_t lds_load(const uint32_t* p) {
@@ -953,88 +954,6 @@ __device__ __forceinline__ void xq_item(const Args& a, int item) {
   }
 }
 
-// The decode block's RMSNorm prologue for one row: x = bf16(h / sqrt(mean(h^2)
-// + eps)) (unit gain), quantized into the workspace as xq_item does, by one
-// wavefront: part `part` of `parts` of the row's 128-column groups (each
-// part forms the row's whole sum of squares itself).  The sum of squares is formed in exactly the order of the
-// standalone RMSNorm kernel (256 partial sums, partial t taking the 16-byte
-// chunks t, t + 256, t + 512, t + 768, then t + 1024, ... in one fma chain;
-// a butterfly over each group of 64 partials; the four group sums added in
-// order), so x is bit-identical to that kernel's output.  Lane l holds
-// partials l, 64 + l, 128 + l and 192 + l.  With `stash` (LDS for d floats)
-// the row read for the sum of squares is kept there for the quantization
-// pass, instead of being read from memory again.
-template <int FMT>
-__device__ __forceinline__ void row_prologue(const Args& a, int row, int part, int parts, float* stash) {
-  const int l = lane_id();
-  const int d = a.K1, n4 = d >> 2, ng = d >> 7;
-  const int jb = 4 * ((part * ng) / parts), je = 4 * (((part + 1) * ng) / parts);  // this part's 32-column blocks
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h_in + (size_t)row * d, (uint32_t)d * 4u);
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < n4; c0 += 1024) {
-    v4f v[4][4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + 64 * w + l + 256 * u;  // (past the row: zeros, which leave the chain unchanged)
-        v[w][u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rh, c < n4 ? (uint32_t)c * 16u : OOB, 0, 0));
-      }
-    if (stash) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = c0 + 64 * w + l + 256 * u;
-          if (c < n4) *reinterpret_cast<v4f*>(stash + 4 * c) = v[w][u];
-        }
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ss[w] = fmaf(v[w][u][e], v[w][u][e], ss[w]);
-  }
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss[w] += __shfl_xor(ss[w], o, WAVE);
-  const float inv = 1.0f / sqrtf((((ss[0] + ss[1]) + ss[2]) + ss[3]) / (float)d + a.eps);
-  // (the stash is written and read by this one wavefront, whose LDS accesses
-  // complete in program order)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  const __amdgpu_buffer_rsrc_t rxa = make_rsrc(a.xa, (uint32_t)a.M * (uint32_t)a.K1);
-  // one lane per 32-column block (jb and je are multiples of 4: the four
-  // lanes of a 128-column group agree on j < je)
-  for (int j0 = jb; j0 < je; j0 += 64) {
-    const int j = j0 + l;
-    if (j < je) {
-      float v[32];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const v4f t = stash ? *reinterpret_cast<const v4f*>(stash + 4 * (8 * j + c))
-                            : __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rh, (uint32_t)(8 * j + c) * 16u, 0, 0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * c + e] = bf16_to_f32(f32_to_bf16(t[e] * inv));
-      }
-      uint32_t cw[8], se = 0;
-      float sf = 1.0f;
-      quant_block32<FMT>(v, cw, &sf, &se);
-      const uint32_t off = act_code_off(a.M, a.K1, row, 32 * j);
-      st_coherent_b128(rxa, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
-      st_coherent_b128(rxa, off + 16u * act_tile_rows(a.M, row), make_uint4(cw[4], cw[5], cw[6], cw[7]));
-      if (FMT == FMT_BLOCK) {
-        if ((j & 3) == 0) st_coherent(static_cast<float*>(a.xs) + (size_t)(j >> 2) * a.Mpad + row, sf);
-      } else {
-        const uint32_t e4 = pack4_lanes(se);
-        if ((j & 3) == 0)
-          st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.xs) + act_scale_off(a.M, a.K1, row, j >> 2)), e4);
-      }
-    }
-  }
-}
-
 // Block-format scales of the padded rows M..Mpad-1 of every group of Q(x): zero.
 __device__ __forceinline__ void zero_pad_x_scales(const Args& a) {
   const int pad = a.Mpad - a.M, KT1 = a.K1 >> 7;
@@ -1097,6 +1016,89 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 __device__ __forceinline__ void raise_flag(uint32_t* ctrl, int page_off, int i, uint32_t ep) {
   const int l = lane_id();
   if (l < NREP) store_agent(&ctrl[PAGE0 + l * PAGE_WORDS + page_off + i], ep);
+}
+
+// The decode block's RMSNorm prologue: x = bf16(h / sqrt(mean(h^2) + eps))
+// (unit gain), quantized into the workspace as xq_item does, by every
+// wavefront of a workgroup before they take up their roles.  Item i is part
+// i % P of the 128-column groups of row i / P (P = row_parts; M * P items
+// dealt over the n_items workgroups); each item forms its row's whole sum of
+// squares.  That sum follows the standalone RMSNorm kernel's order exactly:
+// 256 partial sums, partial t (lane t % 64 of wavefront t / 64, the first
+// four wavefronts) taking the 16-byte chunks t, t + 256, t + 512, t + 768,
+// t + 1024, ... in one fma chain; a butterfly over each wavefront's 64; the
+// four wavefront sums added in order.  So x is bit-identical to that
+// kernel's output.  With `stash` (LDS for K1 floats) the row read for the
+// sum of squares is kept for the quantization pass.  Ends with every
+// wavefront's stores drained and the workgroup's flag raised.
+template <int FMT>
+__device__ __forceinline__ void block_prologue(const Args& a, float* red, float* stash, uint32_t ep) {
+  const int l = lane_id(), wv = (int)(threadIdx.x >> 6), nw = (int)(blockDim.x >> 6);
+  const int W = blockIdx.x, P = a.row_parts;
+  const int d = a.K1, n4 = d >> 2, ng = d >> 7;
+  const __amdgpu_buffer_rsrc_t rxa = make_rsrc(a.xa, (uint32_t)a.M * (uint32_t)a.K1);
+  for (int i = W; i < a.M * P; i += a.n_items) {
+    const int row = i / P, part = i - row * P;
+    const int jb = 4 * ((part * ng) / P), je = 4 * (((part + 1) * ng) / P);  // this part's 32-column blocks
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h_in + (size_t)row * d, (uint32_t)d * 4u);
+    if (wv < 4) {
+      float ss = 0.0f;
+      for (int c0 = 64 * wv + l; c0 < n4 + 64 * wv + l; c0 += 1024) {
+        // (chunks past the row are zeros, which leave the chain unchanged)
+        v4f v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + 256 * u;
+          v[u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rh, c < n4 ? (uint32_t)c * 16u : OOB, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + 256 * u;
+          if (stash && c < n4) *reinterpret_cast<v4f*>(stash + 4 * c) = v[u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = fmaf(v[u][e], v[u][e], ss);
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
+      if (l == 0) red[wv] = ss;
+    }
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((((red[0] + red[1]) + red[2]) + red[3]) / (float)d + a.eps);
+    // one lane per 32-column block over the whole workgroup (jb, je and the
+    // steps are multiples of 4: the four lanes of a 128-column group agree)
+    for (int j0 = jb + 64 * wv; j0 < je; j0 += 64 * nw) {
+      const int j = j0 + l;
+      if (j < je) {
+        float v[32];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const v4f t = stash ? *reinterpret_cast<const v4f*>(stash + 4 * (8 * j + c))
+                              : __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rh, (uint32_t)(8 * j + c) * 16u, 0, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * c + e] = bf16_to_f32(f32_to_bf16(t[e] * inv));
+        }
+        uint32_t cw[8], se = 0;
+        float sf = 1.0f;
+        quant_block32<FMT>(v, cw, &sf, &se);
+        const uint32_t off = act_code_off(a.M, a.K1, row, 32 * j);
+        st_coherent_b128(rxa, off, make_uint4(cw[0], cw[1], cw[2], cw[3]));
+        st_coherent_b128(rxa, off + 16u * act_tile_rows(a.M, row), make_uint4(cw[4], cw[5], cw[6], cw[7]));
+        if (FMT == FMT_BLOCK) {
+          if ((j & 3) == 0) st_coherent(static_cast<float*>(a.xs) + (size_t)(j >> 2) * a.Mpad + row, sf);
+        } else {
+          const uint32_t e4 = pack4_lanes(se);
+          if ((j & 3) == 0)
+            st_coherent(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.xs) + act_scale_off(a.M, a.K1, row, j >> 2)), e4);
+        }
+      }
+    }
+    __syncthreads();  // (the stash and the partial sums are free for the next item)
+  }
+  if (FMT == FMT_BLOCK && W == 0 && wv == 0) zero_pad_x_scales(a);
+  drain_memory();
+  __syncthreads();  // every wavefront's stores have completed
+  if (wv == 0 && W < a.n_items) raise_flag(a.ctrl, PG_XQ, W, ep);
 }
 
 // A cross-workgroup wait has lasted one more pass: true when it must end
@@ -1432,18 +1434,10 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
   const uint32_t ep = launch_epoch(a);
   const Guard gd{&L.abort, a.ctrl, a.budget, ep};
   if (!XL) {
-    // quantize this workgroup's share of x (decode block: its rows, RMSNorm
-    // first), then wait for everyone's
-    if (W < a.n_items) {
-      if (a.h_in) {
-        // item i: part i % P of row i / P (M * P items, dealt over n_items workgroups)
-        for (int i = W; i < a.M * a.row_parts; i += a.n_items)
-          row_prologue<FMT>(a, i / a.row_parts, i % a.row_parts, a.row_parts,
-                            a.row_stash ? reinterpret_cast<float*>(stages) : nullptr);
-        if (FMT == FMT_BLOCK && W == 0) zero_pad_x_scales(a);
-      } else {
-        xq_item<FMT>(a, W);
-      }
+    // quantize this workgroup's share of x, then wait for everyone's
+    // (the decode block's prologue has run already, flag included)
+    if (W < a.n_items && !a.h_in) {
+      xq_item<FMT>(a, W);
       drain_memory();
       raise_flag(a.ctrl, PG_XQ, W, ep);
     }
@@ -1533,6 +1527,8 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     L.abort = 0u;
   }
   __syncthreads();
+  if (MLP && !XL && a.h_in)
+    block_prologue<FMT>(a, L.red, a.row_stash ? reinterpret_cast<float*>(lds_x) : nullptr, launch_epoch(a));
   if (wv == 0) {
     if (XL) {
       XqLocal<FMT> xq;
@@ -1912,10 +1908,11 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.n_items = XL ? 0 : p.n_items;
   if (pr.h_in) {
     // the prologue's items: rows, each split into row_parts shares of its
-    // 128-column groups (as many as the grid has workgroups for)
-    const int ng = pr.K1 / 128;
-    int parts = G / pr.M;
-    if (parts > ng) parts = ng;
+    // 128-column groups, as few as give every lane of a workgroup at most one
+    // 32-column block (each share reads the whole row for its sum of squares)
+    const int ng = pr.K1 / 128, lanes = 64 * cfg_nwave(MT);
+    int parts = (4 * ng + lanes - 1) / lanes;
+    if (parts > G / pr.M) parts = G / pr.M;
     if (parts < 1) parts = 1;
     a.row_parts = parts;
     a.n_items = pr.M * parts < G ? pr.M * parts : G;
