@@ -68,6 +68,7 @@ enum {
 enum { SGD_FMT_BLOCK128 = 1, SGD_FMT_MX32 = 2 };
 
 #define SGD_MAX_M 128 /* largest row count of sgd_scaled_gemm / fused MLP */
+#define SGD_MAX_M_LARGE 65536 /* largest row count of the large-M (prefill) path */
 
 /*
  * A packed (pre-shuffled) FP8 weight W [N, K] in nn.Linear orientation
@@ -280,6 +281,53 @@ int sgd_fused_swiglu_block(const float* h_in, int M, const sgd_weight* gate,
                            const sgd_weight* up, const sgd_weight* down, float eps,
                            float* h_out, void* workspace, size_t ws_bytes,
                            void* stream);
+
+/* ---- large-M (prefill) path: compute-bound tiled GEMMs ------------------ */
+/*
+ * The pages' second benchmark family (fish.audio blog, section "Resultados
+ * de benchmark del kernel": the SwiGLU MLP at M from 1 to 4096, and square
+ * MXFP8 GEMMs from 1024^3 to 16384^3), where the arithmetic intensity (about
+ * M flop per weight byte) puts the matrix cores, not HBM, on the critical
+ * path.  Same quantization, weights and arithmetic as the decode path (the
+ * scaled fp8 MFMA with fp32 accumulation), in an LDS-tiled kernel: blocks
+ * of 256x128 (128x128 when that gives fewer blocks than compute units) of
+ * the output over all of K, two LDS stages.  Several launches each; no
+ * persistent waits.  Their workspaces keep no state between calls and leave
+ * the first 256 KB (a persistent call's control block) untouched, so one
+ * workspace may serve both paths when the calls are serialised.
+ */
+
+/* Workspace of sgd_scaled_gemm_large: Q(x) in 16-row tiles.  0 for an
+ * unsupported shape (M > SGD_MAX_M_LARGE, N or K not multiples of 128, or
+ * 16*ceil(M/16)*K >= 2^31). */
+size_t sgd_gemm_large_workspace_bytes(int fmt, int M, int N, int K);
+
+/* y [M, N] bf16 = Q(x) W^T for x [M, K] bf16, any 1 <= M <= SGD_MAX_M_LARGE:
+ * the result of sgd_scaled_gemm (fish.audio blog, section "Qué hay en código
+ * abierto"), up to the order of the fp32 sums.  Two launches (quantize x,
+ * tiled GEMM).  Errors as sgd_scaled_gemm, workspace
+ * sgd_gemm_large_workspace_bytes. */
+int sgd_scaled_gemm_large(const uint16_t* x_bf16, int M, const sgd_weight* w,
+                          uint16_t* y_bf16, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/* Workspace of sgd_swiglu_mlp_prefill: Q(x), the fp32 gate/up products of
+ * 16*ceil(M/16) rows and Q(a).  0 for an unsupported shape. */
+size_t sgd_mlp_prefill_workspace_bytes(int fmt, int M, int d, int ffn);
+
+/* y [M, d] bf16 = SwiGLU MLP of x [M, d] bf16 for large M (the arithmetic of
+ * sgd_fused_swiglu_mlp, fish.audio blog, section "Qué hay en código
+ * abierto"; X post, section "Custom kernels for the shapes TTS actually
+ * uses"): quantize x; [g | u] = Q(x) [Wg; Wu]^T in fp32 (tiled GEMM);
+ * a = silu(g) * u re-quantized per row; y = Q(a) Wd^T (tiled GEMM).  Four
+ * launches, intermediates in the workspace.  gate_up is the stacked
+ * [2*ffn, d] weight (gate rows first, as sgd_scaled_gemm_f32 of the
+ * unfused pipeline reads it); down is [d, ffn].  1 <= M <= SGD_MAX_M_LARGE.
+ * Errors: SGD_EINVAL, SGD_EALIGN, SGD_EDIM (shapes that do not chain or are
+ * unsupported), SGD_EFMT, SGD_EWORKSPACE. */
+int sgd_swiglu_mlp_prefill(const uint16_t* x_bf16, int M, const sgd_weight* gate_up,
+                           const sgd_weight* down, uint16_t* y_bf16, void* workspace,
+                           size_t ws_bytes, void* stream);
 
 /* ---- the unfused pipeline (three launches, intermediates in HBM) -------- */
 /*

@@ -402,6 +402,57 @@ def unfused_swiglu_mlp(x, gate_up, down, out=None, workspace=None, buffers=None)
     return scaled_gemm_q(aq, sc, M, down, out=out, workspace=workspace)
 
 
+def scaled_gemm_large(x, w, out=None, workspace=None):
+    """y [M, N] bf16 = Q(x) W^T for any 1 <= M <= 65536 (the large-M tiled
+    path: quantize x, then the LDS-tiled fp8 GEMM)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    _need(x, "x", torch.bfloat16, device=w.device)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, weight has K={w.K}")
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (M, w.N), x.device)
+    need = lib().sgd_gemm_large_workspace_bytes(w.fmt, M, w.N, w.K)
+    if need == 0:
+        raise ValueError(f"unsupported large GEMM shape M={M} N={w.N} K={w.K}")
+    st = w.c_struct()
+
+    def launch():
+        ws = _workspace(x.device, need, workspace)
+        _lib.check("sgd_scaled_gemm_large", lib().sgd_scaled_gemm_large(
+            _ptr(x), M, ctypes.byref(st), _ptr(out), _ptr(ws), ws.numel(), _stream(x)))
+    _serialise_persistent(x.device, launch)
+    return out
+
+
+def swiglu_mlp_prefill(x, gate_up, down, out=None, workspace=None):
+    """y [M, d] bf16 = SwiGLU MLP for large M (quantize x, tiled gate/up GEMM
+    into fp32, SwiGLU + re-quantization, tiled down GEMM); gate_up =
+    stack_packed(gate, up)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, d]")
+    _need(x, "x", torch.bfloat16, device=down.device)
+    M, d = x.shape
+    if gate_up.K != d or down.N != d or gate_up.N != 2 * down.K:
+        raise ValueError("weights do not chain with x")
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (M, d), x.device)
+    need = lib().sgd_mlp_prefill_workspace_bytes(down.fmt, M, d, down.K)
+    if need == 0:
+        raise ValueError(f"unsupported prefill MLP shape M={M} d={d} ffn={down.K}")
+    gu, dn = gate_up.c_struct(), down.c_struct()
+
+    def launch():
+        ws = _workspace(x.device, need, workspace)
+        _lib.check("sgd_swiglu_mlp_prefill", lib().sgd_swiglu_mlp_prefill(
+            _ptr(x), M, ctypes.byref(gu), ctypes.byref(dn), _ptr(out), _ptr(ws), ws.numel(), _stream(x)))
+    _serialise_persistent(x.device, launch)
+    return out
+
+
 def fused_swiglu_mlp_noalloc(x, gate, up, down, out):
     """The fused MLP through the entry point that allocates nothing (its
     workspace is the library's fixed per-device array): y [M, d] bf16 into

@@ -50,6 +50,10 @@ SIGNATURES = {
     "sgd_fused_swiglu_mlp": (_i, [_vp, _i, _wp, _wp, _wp, _vp, _vp, _sz, _vp]),
     "sgd_fused_swiglu_mlp_noalloc": (_i, [_vp, _i, _wp, _wp, _wp, _vp, _vp]),
     "sgd_fused_swiglu_block": (_i, [_vp, _i, _wp, _wp, _wp, _f, _vp, _vp, _sz, _vp]),
+    "sgd_gemm_large_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "sgd_scaled_gemm_large": (_i, [_vp, _i, _wp, _vp, _vp, _sz, _vp]),
+    "sgd_mlp_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "sgd_swiglu_mlp_prefill": (_i, [_vp, _i, _wp, _wp, _vp, _vp, _sz, _vp]),
     "sgd_scaled_gemm_f32": (_i, [_vp, _i, _wp, _vp, _vp, _sz, _vp]),
     "sgd_act_scales_bytes": (_sz, [_i, _i, _i]),
     "sgd_swiglu_quantize": (_i, [_i, _vp, _i, _i, _vp, _vp, _vp]),

@@ -310,6 +310,86 @@ int sgd_fused_swiglu_block(const float* h_in, int M, const sgd_weight* gate, con
   return launch_stream(p, as_stream(stream));
 }
 
+// ---- large-M (prefill) path ----
+namespace {
+inline size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
+// Rows past which the 32-bit offsets of the tiled kernels would overflow.
+bool large_shape_ok(int M, int K) {
+  const size_t Mpad = (size_t)((M + 15) / 16) * 16;
+  return Mpad * (size_t)K < ((size_t)1 << 31);
+}
+}  // namespace
+
+size_t sgd_gemm_large_workspace_bytes(int fmt, int M, int N, int K) {
+  if (!fmt_ok(fmt) || M <= 0 || M > SGD_MAX_M_LARGE || N <= 0 || K <= 0 || N > MAX_DIM || K > MAX_DIM) return 0;
+  if ((N % 128) || (K % 128) || !large_shape_ok(M, K)) return 0;
+  return CONTROL_BLOCK_BYTES + a256(act_tiles_codes_bytes(M, K)) + a256(act_tiles_scales_bytes(fmt, M, K));
+}
+
+int sgd_scaled_gemm_large(const uint16_t* x_bf16, int M, const sgd_weight* w, uint16_t* y_bf16, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (!x_bf16 || !y_bf16 || M <= 0 || M > SGD_MAX_M_LARGE) return SGD_EINVAL;
+  if (!al16(x_bf16) || !al16(y_bf16)) return SGD_EALIGN;
+  if (!workspace) return SGD_EWORKSPACE;
+  if (!al16(workspace)) return SGD_EALIGN;
+  const size_t need = sgd_gemm_large_workspace_bytes(w->fmt, M, w->N, w->K);
+  if (need == 0) return SGD_EDIM;
+  if (ws_bytes < need) return SGD_EWORKSPACE;
+  // (the first CONTROL_BLOCK_BYTES are left alone: a workspace may be shared
+  // with the persistent entry points, whose control block lives there)
+  uint8_t* ws = static_cast<uint8_t*>(workspace) + CONTROL_BLOCK_BYTES;
+  uint8_t* codes = ws;
+  void* scales = ws + a256(act_tiles_codes_bytes(M, w->K));
+  hipStream_t s = as_stream(stream);
+  rc = launch_act_tiles(w->fmt, x_bf16, M, w->K, codes, scales, s);
+  if (rc) return rc;
+  return launch_tile_gemm(w->fmt, codes, scales, M, w->K, w, y_bf16, false, s);
+}
+
+size_t sgd_mlp_prefill_workspace_bytes(int fmt, int M, int d, int ffn) {
+  if (!fmt_ok(fmt) || M <= 0 || M > SGD_MAX_M_LARGE || d <= 0 || ffn <= 0 || d > MAX_DIM || ffn > 32768) return 0;
+  if ((d % 128) || (ffn % 128) || !large_shape_ok(M, d) || !large_shape_ok(M, 2 * ffn)) return 0;
+  const size_t Mpad = (size_t)((M + 15) / 16) * 16;
+  return CONTROL_BLOCK_BYTES + a256(act_tiles_codes_bytes(M, d)) + a256(act_tiles_scales_bytes(fmt, M, d)) +
+         a256(Mpad * 2 * ffn * 4) + a256(act_tiles_codes_bytes(M, ffn)) + a256(act_tiles_scales_bytes(fmt, M, ffn));
+}
+
+int sgd_swiglu_mlp_prefill(const uint16_t* x_bf16, int M, const sgd_weight* gate_up, const sgd_weight* down,
+                           uint16_t* y_bf16, void* workspace, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_weight(gate_up)) || (rc = check_weight(down))) return rc;
+  if (gate_up->fmt != down->fmt) return SGD_EFMT;
+  const int fmt = down->fmt, d = down->N, F = down->K;
+  if (gate_up->N != 2 * F || gate_up->K != d) return SGD_EDIM;
+  if (!x_bf16 || !y_bf16 || M <= 0 || M > SGD_MAX_M_LARGE) return SGD_EINVAL;
+  if (!al16(x_bf16) || !al16(y_bf16)) return SGD_EALIGN;
+  if (!workspace) return SGD_EWORKSPACE;
+  if (!al16(workspace)) return SGD_EALIGN;
+  const size_t need = sgd_mlp_prefill_workspace_bytes(fmt, M, d, F);
+  if (need == 0) return SGD_EDIM;
+  if (ws_bytes < need) return SGD_EWORKSPACE;
+  const int Mpad = (M + 15) / 16 * 16;
+  uint8_t* p = static_cast<uint8_t*>(workspace) + CONTROL_BLOCK_BYTES;  // (control block untouched)
+  uint8_t* xq = p;
+  p += a256(act_tiles_codes_bytes(M, d));
+  void* xs = p;
+  p += a256(act_tiles_scales_bytes(fmt, M, d));
+  float* gu = reinterpret_cast<float*>(p);
+  p += a256((size_t)Mpad * 2 * F * 4);
+  uint8_t* aq = p;
+  p += a256(act_tiles_codes_bytes(M, F));
+  void* as = p;
+  hipStream_t s = as_stream(stream);
+  // Q(x); [g | u] = Q(x) [Wg; Wu]^T in fp32 for all Mpad rows (padded rows
+  // are zero); Q(silu(g) * u); y = Q(a) Wd^T for the M rows
+  if ((rc = launch_act_tiles(fmt, x_bf16, M, d, xq, xs, s))) return rc;
+  if ((rc = launch_tile_gemm(fmt, xq, xs, Mpad, d, gate_up, gu, true, s))) return rc;
+  if ((rc = launch_swiglu_quantize_tiles(fmt, gu, Mpad, F, aq, as, s))) return rc;
+  return launch_tile_gemm(fmt, aq, as, M, F, down, y_bf16, false, s);
+}
+
 int sgd_bf16_to_f32(const uint16_t* x_bf16, int M, int d, float* h, void* stream) {
   if (!x_bf16 || !h || M <= 0 || d <= 0 || M > 65536 || d > MAX_DIM) return SGD_EINVAL;
   if (d % 128) return SGD_EDIM;

@@ -48,6 +48,14 @@ int stream_workspace_layout(int fmt, int M, int K1, int F, size_t (&off)[5]);
 int act_mtile_pad(int M);
 // a = silu(g) * u from gu [M, 2F] fp32, quantized into the workspace layout.
 int launch_swiglu_quantize(int fmt, const float* gu, int M, int F, uint8_t* aq, void* as, hipStream_t s);
+int launch_swiglu_quantize_tiles(int fmt, const float* gu, int Mrows, int F, uint8_t* aq, void* as, hipStream_t s);
+// Large-M path: Q(x) of bf16 x [M, K] in the full-tile activation layout
+// (Mpad = 16*ceil(M/16) rows), and C = Q(A) W^T from that layout.
+size_t act_tiles_codes_bytes(int M, int K);
+size_t act_tiles_scales_bytes(int fmt, int M, int K);
+int launch_act_tiles(int fmt, const uint16_t* x, int M, int K, uint8_t* codes, void* scales, hipStream_t s);
+int launch_tile_gemm(int fmt, const uint8_t* a, const void* as, int M, int K, const sgd_weight* w, void* c,
+                     bool out_f32, hipStream_t s);
 int launch_stream(const Problem& p, hipStream_t s);
 
 // Host-side validation of a fused-MLP call's arguments other than its

@@ -1,0 +1,330 @@
+// Large-M (prefill) path: the scaled fp8 GEMM as a compute-bound tiled
+// kernel, for M beyond the decode shapes of the streaming kernel.  The pages'
+// second benchmark family (fish.audio blog, section "Resultados de benchmark
+// del kernel": the MLP at M from 1 to 4096 and square MXFP8 GEMMs from 1024^3
+// to 16384^3) is this regime: arithmetic intensity ~M flop per weight byte,
+// far above the HBM ridge, so the matrix cores set the pace.
+//
+// Operands.  Both are arrays of 2 KB tiles in the operand order of
+// v_mfma_scale_f32_16x16x128_f8f6f4 (lane l = r + 16q: row r, columns
+// 16q..16q+15 at byte 16l and 64+16q.. at 1024 + 16l):
+//   * the packed weight, tile (n-block j, k-tile t) at (j*K/128 + t)*2048;
+//   * the activations in the workspace layout with every m-tile full
+//     (M padded to Mpad = 16*ceil(M/16) zero rows): tile (m-tile i, k-tile t)
+//     at i*16*K + t*2048.
+// So a workgroup copies whole tiles from memory to LDS and each wavefront
+// reads its operands with two 16-byte LDS reads per tile.
+//
+// Kernel.  A workgroup computes a BM x BN block of C = Q(x) W^T over all of
+// K, k-tile by k-tile through two LDS stages: while the matrix cores work on
+// stage kt, k-tile kt+1 is copied into the other stage by direct
+// memory-to-LDS loads (no registers; waited for before the one barrier per
+// k-tile).  Wavefront
+// (wm, wn) owns TM m-tiles x TN n-blocks.  MX: the E8M0 scales go into the
+// instruction; block format: the unscaled product of each k-tile is added
+// with the row's activation scale times the weight block's scale, as in the
+// streaming kernel.
+#include "sgd_act.hpp"
+#include "sgd_device.hpp"
+#include "sgd_host.hpp"
+
+namespace sgd {
+
+namespace {
+
+constexpr uint32_t OOB_T = 0x80000000u;  // a buffer offset past every buffer's end
+
+struct TileArgs {
+  const uint8_t* a;  // Q(x) codes, full m-tiles [Mpad/16][K/128][2048]
+  const void* as;    // block: fp32 [K/128][Mpad]; mx: [Mpad/16][K/128][16] dwords
+  int Mpad, K;
+  const uint8_t* w;  // packed weight [N/16][K/128][2048]
+  const void* ws;    // packed weight scales
+  int N;
+  void* c;           // [M, N] bf16 or fp32 (row-major)
+  int M;             // rows of C stored
+  uint32_t a_bytes, as_bytes, w_bytes, ws_bytes;
+  int tiles_m;       // blocks along M (the grid is tiles_m x blocks along N)
+};
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ int uni_t(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// 1 KB from memory straight into LDS: lane l's 16 bytes at buffer offset
+// voff land at LDS byte m0 + 16*l.  Written as the instruction itself so that
+// the compiler does not wait for it before unrelated LDS reads; the kernel
+// waits for these copies itself (lds_copies_done) before its barrier.  No
+// register receives data.
+__device__ __forceinline__ void lds_copy1k(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copies_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int FMT, int WGM, int WGN, int TM, int TN, int OUT>
+__global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
+  constexpr int NT = 64 * WGM * WGN;      // threads
+  constexpr int AT = WGM * TM, BT = WGN * TN;  // A and B tiles of a stage
+  constexpr int ST = AT + BT;
+  constexpr int NW = WGM * WGN;
+  constexpr int CH = 2 * ST / NW;         // 1 KB halves of tiles each wavefront copies per stage
+  static_assert(2 * ST % NW == 0, "stage halves");
+  extern __shared__ __align__(16) uint8_t lds[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds;
+  const int l = lane_id(), wv = uni_t((int)(threadIdx.x >> 6));
+  const int wm = wv % WGM, wn = wv / WGM;
+  const int bm = blockIdx.x % p.tiles_m, bn = blockIdx.x / p.tiles_m;
+  const int KT = p.K >> 7;
+  const int mt0 = bm * AT, nb0 = bn * BT;  // first m-tile / n-block of the block
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes), rw = make_rsrc(p.w, p.w_bytes);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(p.as, p.as_bytes), rws = make_rsrc(p.ws, p.ws_bytes);
+  const int MTA = p.Mpad >> 4, NBW = p.N >> 4;
+
+  // ---- stage copy: wavefront wv copies halves wv, wv + NW, ... of the
+  // stage's ST tiles (tiles past the matrices read zeros) ----
+  auto copy_stage = [&](int kt, int s) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int h = wv + NW * i, t = h >> 1, half = h & 1;
+      const uint32_t m0 = lds0 + (uint32_t)((s * ST + t) * 2048 + half * 1024);
+      const uint32_t lo = (uint32_t)half * 1024u + (uint32_t)l * 16u;
+      if (t < AT) {
+        const int mt = mt0 + t;
+        lds_copy1k(ra, m0, mt < MTA ? (uint32_t)mt * 16u * (uint32_t)p.K + (uint32_t)kt * 2048u + lo : OOB_T);
+      } else {
+        const int nb = nb0 + t - AT;
+        lds_copy1k(rw, m0, nb < NBW ? ((uint32_t)nb * (uint32_t)KT + (uint32_t)kt) * 2048u + lo : OOB_T);
+      }
+    }
+  };
+
+  // ---- this wavefront's scales for one k-tile ----
+  // mx: the activation scale byte of (row l%16, block l/16) per m-tile, and
+  // the weight's dword of 4 k-tiles per n-block (the k-tile's byte selected
+  // at use); block: the activation scales of rows 4(l/16)..+3 per m-tile and
+  // the 128x128 weight block's scale (one per wavefront: TN*16 <= 128 rows
+  // aligned to 128).
+  struct Scales {
+    uint32_t xa[TM];
+    v4f xb[TM];
+    uint32_t wsd[TN];
+    float wbs;
+  };
+  auto load_scales = [&](int kt, Scales& sc) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int mt = mt0 + wm * TM + i;
+      const bool ok = mt < MTA;
+      if (FMT == FMT_MX) {
+        const uint32_t o = (uint32_t)mt * 16u * (uint32_t)(p.K >> 5) + (uint32_t)kt * 64u + (uint32_t)(l & 15) * 4u +
+                           (uint32_t)(l >> 4);
+        sc.xa[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ras, ok ? o : OOB_T, 0, 0);
+      } else {
+        const uint32_t o = ((uint32_t)kt * (uint32_t)p.Mpad + (uint32_t)mt * 16u + 4u * (uint32_t)(l >> 4)) * 4u;
+        sc.xb[i] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(ras, ok ? o : OOB_T, 0, 0));
+      }
+    }
+    if (FMT == FMT_MX) {
+      const uint32_t KG = (uint32_t)(KT + 3) >> 2;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int nb = nb0 + wn * TN + j;
+        const uint32_t o = ((uint32_t)nb * KG + (uint32_t)(kt >> 2)) * 256u + (uint32_t)l * 4u;
+        sc.wsd[j] = __builtin_amdgcn_raw_buffer_load_b32(rws, nb < NBW ? o : OOB_T, 0, 0);
+      }
+    } else {
+      const int nb = nb0 + wn * TN;
+      const uint32_t o = ((uint32_t)(nb >> 3) * (uint32_t)KT + (uint32_t)kt) * 4u;
+      sc.wbs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rws, nb < NBW ? o : OOB_T, 0, 0));
+    }
+  };
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  Scales sc_cur, sc_next;
+  copy_stage(0, 0);
+  load_scales(0, sc_cur);
+  lds_copies_done();
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool more = kt + 1 < KT;
+    if (more) {
+      // (the other stage was last read in the previous k-tile, before its barrier)
+      copy_stage(kt + 1, (kt + 1) & 1);
+      load_scales(kt + 1, sc_next);
+    }
+    const uint8_t* st = lds + (kt & 1) * ST * 2048;
+    v8i av[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint8_t* t = st + (wm * TM + i) * 2048 + l * 16;
+      av[i] = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
+    }
+    const int sh = 8 * (kt & 3);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const uint8_t* t = st + (AT + wn * TN + j) * 2048 + l * 16;
+      const v8i bv = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (FMT == FMT_MX) {
+          acc[i][j] = mfma_f8(av[i], bv, acc[i][j], (int)sc_cur.xa[i], (int)(sc_cur.wsd[j] >> sh));
+        } else {
+          const v4f z = {0.f, 0.f, 0.f, 0.f};
+          const v4f t4 = mfma_f8(av[i], bv, z, 127, 127);
+          acc[i][j] += t4 * (sc_cur.xb[i] * sc_cur.wbs);
+        }
+      }
+    }
+    lds_copies_done();
+    __syncthreads();
+    if (more) sc_cur = sc_next;
+  }
+
+  // ---- epilogue: rows < M, columns < N ----
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = (nb0 + wn * TN + j) * 16 + (l & 15);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = (mt0 + wm * TM + i) * 16 + 4 * (l >> 4) + rr;
+        if (row < p.M && col < p.N) {
+          const size_t o = (size_t)row * p.N + col;
+          if (OUT == 1)
+            static_cast<float*>(p.c)[o] = acc[i][j][rr];
+          else
+            static_cast<uint16_t*>(p.c)[o] = (uint16_t)f32_to_bf16(acc[i][j][rr]);
+        }
+      }
+    }
+}
+
+// Q(x) of bf16 x [M, K] in the workspace layout with full m-tiles (rows
+// M..Mpad-1 quantized as zeros): one wavefront per (m-tile, 128-column
+// group), one lane per (row, 32-column block), the streaming kernel's
+// quantizer.
+template <int FMT>
+__global__ __launch_bounds__(256) void act_tiles_kernel(const uint16_t* __restrict__ x, int M, int K, int Mpad,
+                                                        uint8_t* __restrict__ codes, void* __restrict__ scales) {
+  const int nmt = Mpad >> 4, ng = K >> 7;
+  const long long wave = ((long long)blockIdx.x * 256 + threadIdx.x) >> 6;
+  if (wave >= (long long)nmt * ng) return;
+  const int g = (int)(wave / nmt), mt = (int)(wave - (long long)g * nmt);
+  const int l = lane_id(), row = mt * 16 + (l >> 2), j = l & 3;
+  float v[32];
+  if (row < M) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)row * K + g * 128 + 32 * j);
+    uint4 w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = src[c];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * c + 2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
+        v[8 * c + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) v[e] = 0.0f;
+  }
+  uint32_t cw[8], se = 0;
+  float sf = 1.0f;
+  quant_block32<FMT>(v, cw, &sf, &se);
+  const size_t off = (size_t)mt * 16 * K + (size_t)(g * 128 + 32 * j) / 16 * 256 + (size_t)(l >> 2) * 16;
+  *reinterpret_cast<uint4*>(codes + off) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+  *reinterpret_cast<uint4*>(codes + off + 256) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+  if (FMT == FMT_BLOCK) {
+    // (padded rows: zero scales, like the streaming kernel's layout)
+    if (j == 0) static_cast<float*>(scales)[(size_t)g * Mpad + row] = row < M ? sf : 0.0f;
+  } else {
+    const uint32_t e4 = pack4_lanes(se);
+    if (j == 0)
+      reinterpret_cast<uint32_t*>(scales)[(size_t)mt * 16 * (K >> 5) / 4 + (size_t)g * 16 + (l >> 2)] = e4;
+  }
+}
+
+template <int FMT, int OUT>
+int launch_tile_gemm_fmt(const TileArgs& a, bool big, hipStream_t s) {
+  TileArgs p = a;
+  if (big) {
+    // 256 x 128 blocks, 8 wavefronts of 64 x 64
+    constexpr int WGM = 4, WGN = 2, TM = 4, TN = 4;
+    constexpr int BM = WGM * TM * 16, BN = WGN * TN * 16;
+    constexpr size_t lds = 2 * (size_t)(WGM * TM + WGN * TN) * 2048;
+    p.tiles_m = (p.Mpad + BM - 1) / BM;
+    const long long grid = (long long)p.tiles_m * ((p.N + BN - 1) / BN);
+    auto k = tile_gemm_kernel<FMT, WGM, WGN, TM, TN, OUT>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+        hipSuccess)
+      return SGD_EHIP;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * WGM * WGN), lds, s, p);
+  } else {
+    // 128 x 128 blocks, 4 wavefronts of 64 x 64
+    constexpr int WGM = 2, WGN = 2, TM = 4, TN = 4;
+    constexpr int BM = WGM * TM * 16, BN = WGN * TN * 16;
+    constexpr size_t lds = 2 * (size_t)(WGM * TM + WGN * TN) * 2048;
+    p.tiles_m = (p.Mpad + BM - 1) / BM;
+    const long long grid = (long long)p.tiles_m * ((p.N + BN - 1) / BN);
+    auto k = tile_gemm_kernel<FMT, WGM, WGN, TM, TN, OUT>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+        hipSuccess)
+      return SGD_EHIP;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * WGM * WGN), lds, s, p);
+  }
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace
+
+size_t act_tiles_codes_bytes(int M, int K) { return (size_t)((M + 15) / 16) * 16 * (size_t)K; }
+size_t act_tiles_scales_bytes(int fmt, int M, int K) {
+  const size_t Mpad = (size_t)((M + 15) / 16) * 16;
+  return fmt == FMT_BLOCK ? (size_t)(K / 128) * Mpad * 4 : Mpad * (size_t)(K / 32);
+}
+
+int launch_act_tiles(int fmt, const uint16_t* x, int M, int K, uint8_t* codes, void* scales, hipStream_t s) {
+  const int Mpad = (M + 15) / 16 * 16;
+  const long long waves = (long long)(Mpad / 16) * (K / 128);
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (fmt == FMT_BLOCK)
+    hipLaunchKernelGGL(act_tiles_kernel<FMT_BLOCK>, grid, dim3(256), 0, s, x, M, K, Mpad, codes, scales);
+  else
+    hipLaunchKernelGGL(act_tiles_kernel<FMT_MX>, grid, dim3(256), 0, s, x, M, K, Mpad, codes, scales);
+  return hip_status(hipGetLastError());
+}
+
+// C [M, N] (bf16, or fp32 when out_f32) = Q(A) W^T for Q(A) in the full-tile
+// workspace layout of Mpad >= M rows.
+int launch_tile_gemm(int fmt, const uint8_t* a, const void* as, int M, int K, const sgd_weight* w, void* c,
+                     bool out_f32, hipStream_t s) {
+  TileArgs p{};
+  p.a = a;
+  p.as = as;
+  p.Mpad = (M + 15) / 16 * 16;
+  p.K = K;
+  p.w = static_cast<const uint8_t*>(w->codes);
+  p.ws = w->scales;
+  p.N = w->N;
+  p.c = c;
+  p.M = M;
+  p.a_bytes = (uint32_t)act_tiles_codes_bytes(M, K);
+  p.as_bytes = (uint32_t)act_tiles_scales_bytes(fmt, M, K);
+  p.w_bytes = (uint32_t)((size_t)w->N * (size_t)K);
+  p.ws_bytes = (uint32_t)sgd_packed_scales_bytes(fmt, w->N, K);
+  // the big blocks when they still give at least one per compute unit
+  const long long big_blocks = (long long)((p.Mpad + 255) / 256) * ((p.N + 127) / 128);
+  const bool big = big_blocks >= 256;
+  if (fmt == FMT_BLOCK)
+    return out_f32 ? launch_tile_gemm_fmt<FMT_BLOCK, 1>(p, big, s) : launch_tile_gemm_fmt<FMT_BLOCK, 0>(p, big, s);
+  return out_f32 ? launch_tile_gemm_fmt<FMT_MX, 1>(p, big, s) : launch_tile_gemm_fmt<FMT_MX, 0>(p, big, s);
+}
+
+}  // namespace sgd
