@@ -47,7 +47,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_mlp_d4096_ffn12288_mx_m16_traffic.txt")
 FROZEN_FILE = os.path.join(ROOT, "bench_frozen.json")
-KERNEL_SOURCES = ["swiglu_decode_amd/csrc/stream.hip", "swiglu_decode_amd/csrc/sgd_device.hpp"]
+KERNEL_SOURCES = ["swiglu_decode_amd/csrc/stream.hip", "swiglu_decode_amd/csrc/sgd_device.hpp",
+                  "swiglu_decode_amd/csrc/sgd_act.hpp"]
 REGRESSION_TOL = 0.05
 
 
@@ -316,6 +317,68 @@ def bench_stack(torch, sgd, dev, steps, warmup):
     return out
 
 
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak
+
+
+def bench_large(torch, sgd, dev):
+    """The large-M (prefill) path, MFMA-bound: square scaled GEMMs S^3
+    (x [S, S] bf16 quantized per row, packed [S, S] weight; 2 S^3 flop per
+    call) and the prefill SwiGLU MLP at d=4096, ffn=12288 (6 M d ffn flop).
+    Each call includes its x quantization.  Seeded synthetic inputs (x
+    N(0,1), weights N(0,0.02)); timed with HIP events on the stream."""
+
+    def timed(fn, n):
+        s = torch.cuda.current_stream()
+        fn()
+        s.synchronize()
+        times = []
+        for _ in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        return times
+
+    def entry(flop, times):
+        us = sum(times) / len(times)
+        tf = flop / us / 1e6
+        return dict(us_per_call=round(us, 2), p10_p50_p90=[pct(times, 10), pct(times, 50), pct(times, 90)],
+                    tflops=round(tf, 1), roofline=dict(bound="mfma", achieved=round(tf, 1), peak=FP8_PEAK_TFLOPS,
+                                                       unit="TFLOP/s", frac=round(tf / FP8_PEAK_TFLOPS, 4)))
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(1007)
+    out = {}
+    for fmt, sizes in (("mx", (1024, 2048, 4096, 8192, 16384)), ("block", (4096, 8192))):
+        for S in sizes:
+            x = torch.randn((S, S), device=dev, generator=g).to(torch.bfloat16)
+            w = sgd.quantize_pack_weight((torch.randn((S, S), device=dev, generator=g) * 0.02).to(torch.bfloat16), fmt)
+            y = torch.empty((S, S), dtype=torch.bfloat16, device=dev)
+            ws = sgd.Workspace(dev, sgd.lib().sgd_gemm_large_workspace_bytes(sgd.fmt_code(fmt), S, S, S))
+            t = timed(lambda: sgd.scaled_gemm_large(x, w, out=y, workspace=ws), 5 if S >= 8192 else 20)
+            out[f"gemm_{fmt}_{S}^3"] = entry(2.0 * S ** 3, t)
+            del x, w, y, ws
+            torch.cuda.empty_cache()
+    d, F = 4096, 12288
+    for fmt, ms in (("mx", (512, 1024, 4096)), ("block", (4096,))):
+        pw = [sgd.quantize_pack_weight((torch.randn(s, device=dev, generator=g) * 0.02).to(torch.bfloat16), fmt)
+              for s in ((F, d), (F, d), (d, F))]
+        gu = sgd.stack_packed(pw[0], pw[1])
+        for M in ms:
+            x = torch.randn((M, d), device=dev, generator=g).to(torch.bfloat16)
+            y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+            ws = sgd.Workspace(dev, sgd.lib().sgd_mlp_prefill_workspace_bytes(sgd.fmt_code(fmt), M, d, F))
+            t = timed(lambda: sgd.swiglu_mlp_prefill(x, gu, pw[2], out=y, workspace=ws), 10)
+            out[f"prefill_mlp_d{d}_ffn{F}_{fmt}_M{M}"] = entry(6.0 * M * d * F, t)
+            del x, y, ws
+        del pw, gu
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, ms, fmt, y_out, budget_s=10.0):
     """Time the CPU oracle (as it stands) on a bounded sample: passes of one
     MLP call at M=1 and one at M=16 on the headline workload, repeated until
@@ -397,6 +460,8 @@ def main():
                     help="skip the plain streaming-read measurement (profiling runs of the fused kernel)")
     ap.add_argument("--only-main", action="store_true",
                     help="time the headline workload only (no per_config, unfused or warm figures): profiling runs")
+    ap.add_argument("--large", action="store_true",
+                    help="only the large-M path (square scaled GEMMs, prefill MLP)")
     ap.add_argument("--stack", action="store_true",
                     help="only the 24-block decode step (d=2560, ffn=9728, block fp8, M=64, bf16 head)")
     ap.add_argument("--freeze-from", default=None,
@@ -443,6 +508,9 @@ def main():
 
     if args.stack:
         print(json.dumps(bench_stack(torch, sgd, dev, args.steps, args.warmup)))
+        return
+    if args.large:
+        print(json.dumps(bench_large(torch, sgd, dev)))
         return
 
     ms = [int(m) for m in args.ms.split(",")]
@@ -495,6 +563,7 @@ def main():
         del c1
         torch.cuda.empty_cache()
         per_config["decode_stack_d2560_ffn9728_m64"] = bench_stack(torch, sgd, dev, args.steps, args.warmup)
+        per_config["large_m"] = bench_large(torch, sgd, dev)
 
     ceiling = None if args.no_read_ceiling else read_ceiling(dev)
 

@@ -60,11 +60,10 @@ __device__ __forceinline__ void lds_copy1k(__amdgpu_buffer_rsrc_t r, uint32_t m0
 }
 __device__ __forceinline__ void lds_copies_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int FMT, int WGM, int WGN, int TM, int TN, int OUT>
+template <int FMT, int WGM, int WGN, int TM, int TN, int KS, int OUT>
 __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
-  constexpr int NT = 64 * WGM * WGN;      // threads
-  constexpr int AT = WGM * TM, BT = WGN * TN;  // A and B tiles of a stage
-  constexpr int ST = AT + BT;
+  constexpr int AT = WGM * TM, BT = WGN * TN;  // A and B tiles of one k-tile
+  constexpr int ST = KS * (AT + BT);           // tiles of a stage (KS k-tiles)
   constexpr int NW = WGM * WGN;
   constexpr int CH = 2 * ST / NW;         // 1 KB halves of tiles each wavefront copies per stage
   static_assert(2 * ST % NW == 0, "stage halves");
@@ -80,14 +79,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
   const int MTA = p.Mpad >> 4, NBW = p.N >> 4;
 
   // ---- stage copy: wavefront wv copies halves wv, wv + NW, ... of the
-  // stage's ST tiles (tiles past the matrices read zeros) ----
-  auto copy_stage = [&](int kt, int s) {
+  // stage's ST tiles: k-tile kt0 + u of the stage holds tiles
+  // u*(AT+BT) .. (u+1)*(AT+BT)-1, A first (tiles past the matrices, or k-tiles
+  // past K, read zeros) ----
+  auto copy_stage = [&](int kt0, int s) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int h = wv + NW * i, t = h >> 1, half = h & 1;
-      const uint32_t m0 = lds0 + (uint32_t)((s * ST + t) * 2048 + half * 1024);
+      const int h = wv + NW * i, tt = h >> 1, half = h & 1;
+      const int u = tt / (AT + BT), t = tt - u * (AT + BT), kt = kt0 + u;
+      const uint32_t m0 = lds0 + (uint32_t)((s * ST + tt) * 2048 + half * 1024);
       const uint32_t lo = (uint32_t)half * 1024u + (uint32_t)l * 16u;
-      if (t < AT) {
+      if (kt >= KT) {
+        lds_copy1k(ra, m0, OOB_T);
+      } else if (t < AT) {
         const int mt = mt0 + t;
         lds_copy1k(ra, m0, mt < MTA ? (uint32_t)mt * 16u * (uint32_t)p.K + (uint32_t)kt * 2048u + lo : OOB_T);
       } else {
@@ -144,44 +148,56 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  Scales sc_cur, sc_next;
+  Scales sc_cur[KS], sc_next[KS];
   copy_stage(0, 0);
-  load_scales(0, sc_cur);
+#pragma unroll
+  for (int u = 0; u < KS; ++u) load_scales(u, sc_cur[u]);
   lds_copies_done();
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
+  for (int kt0 = 0; kt0 < KT; kt0 += KS) {
+    const bool more = kt0 + KS < KT;
     if (more) {
-      // (the other stage was last read in the previous k-tile, before its barrier)
-      copy_stage(kt + 1, (kt + 1) & 1);
-      load_scales(kt + 1, sc_next);
-    }
-    const uint8_t* st = lds + (kt & 1) * ST * 2048;
-    v8i av[TM];
+      // (the other stage was last read in the previous stage's k-tiles, before its barrier)
+      copy_stage(kt0 + KS, (kt0 / KS + 1) & 1);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const uint8_t* t = st + (wm * TM + i) * 2048 + l * 16;
-      av[i] = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
+      for (int u = 0; u < KS; ++u) load_scales(kt0 + KS + u, sc_next[u]);
     }
-    const int sh = 8 * (kt & 3);
+    const uint8_t* st0 = lds + ((kt0 / KS) & 1) * ST * 2048;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const uint8_t* t = st + (AT + wn * TN + j) * 2048 + l * 16;
-      const v8i bv = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
+    for (int u = 0; u < KS; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= KT) break;
+      const uint8_t* st = st0 + u * (AT + BT) * 2048;
+      const Scales& sc = sc_cur[u];
+      v8i av[TM];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        if (FMT == FMT_MX) {
-          acc[i][j] = mfma_f8(av[i], bv, acc[i][j], (int)sc_cur.xa[i], (int)(sc_cur.wsd[j] >> sh));
-        } else {
-          const v4f z = {0.f, 0.f, 0.f, 0.f};
-          const v4f t4 = mfma_f8(av[i], bv, z, 127, 127);
-          acc[i][j] += t4 * (sc_cur.xb[i] * sc_cur.wbs);
+        const uint8_t* t = st + (wm * TM + i) * 2048 + l * 16;
+        av[i] = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
+      }
+      const int sh = 8 * (kt & 3);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* t = st + (AT + wn * TN + j) * 2048 + l * 16;
+        const v8i bv = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if (FMT == FMT_MX) {
+            acc[i][j] = mfma_f8(av[i], bv, acc[i][j], (int)sc.xa[i], (int)(sc.wsd[j] >> sh));
+          } else {
+            const v4f z = {0.f, 0.f, 0.f, 0.f};
+            const v4f t4 = mfma_f8(av[i], bv, z, 127, 127);
+            acc[i][j] += t4 * (sc.xb[i] * sc.wbs);
+          }
         }
       }
     }
     lds_copies_done();
     __syncthreads();
-    if (more) sc_cur = sc_next;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < KS; ++u) sc_cur[u] = sc_next[u];
+    }
   }
 
   // ---- epilogue: rows < M, columns < N ----
@@ -251,35 +267,24 @@ __global__ __launch_bounds__(256) void act_tiles_kernel(const uint16_t* __restri
   }
 }
 
+template <int FMT, int WGM, int WGN, int TM, int TN, int KS, int OUT>
+int launch_tile_cfg(TileArgs p, hipStream_t s) {
+  constexpr int BM = WGM * TM * 16, BN = WGN * TN * 16;
+  constexpr size_t lds = 2 * (size_t)KS * (WGM * TM + WGN * TN) * 2048;
+  p.tiles_m = (p.Mpad + BM - 1) / BM;
+  const long long grid = (long long)p.tiles_m * ((p.N + BN - 1) / BN);
+  auto k = tile_gemm_kernel<FMT, WGM, WGN, TM, TN, KS, OUT>;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+      hipSuccess)
+    return SGD_EHIP;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * WGM * WGN), lds, s, p);
+  return hip_status(hipGetLastError());
+}
+
 template <int FMT, int OUT>
 int launch_tile_gemm_fmt(const TileArgs& a, bool big, hipStream_t s) {
-  TileArgs p = a;
-  if (big) {
-    // 256 x 128 blocks, 8 wavefronts of 64 x 64
-    constexpr int WGM = 4, WGN = 2, TM = 4, TN = 4;
-    constexpr int BM = WGM * TM * 16, BN = WGN * TN * 16;
-    constexpr size_t lds = 2 * (size_t)(WGM * TM + WGN * TN) * 2048;
-    p.tiles_m = (p.Mpad + BM - 1) / BM;
-    const long long grid = (long long)p.tiles_m * ((p.N + BN - 1) / BN);
-    auto k = tile_gemm_kernel<FMT, WGM, WGN, TM, TN, OUT>;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-        hipSuccess)
-      return SGD_EHIP;
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * WGM * WGN), lds, s, p);
-  } else {
-    // 128 x 128 blocks, 4 wavefronts of 64 x 64
-    constexpr int WGM = 2, WGN = 2, TM = 4, TN = 4;
-    constexpr int BM = WGM * TM * 16, BN = WGN * TN * 16;
-    constexpr size_t lds = 2 * (size_t)(WGM * TM + WGN * TN) * 2048;
-    p.tiles_m = (p.Mpad + BM - 1) / BM;
-    const long long grid = (long long)p.tiles_m * ((p.N + BN - 1) / BN);
-    auto k = tile_gemm_kernel<FMT, WGM, WGN, TM, TN, OUT>;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-        hipSuccess)
-      return SGD_EHIP;
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * WGM * WGN), lds, s, p);
-  }
-  return hip_status(hipGetLastError());
+  if (big) return launch_tile_cfg<FMT, 4, 2, 4, 4, 1, OUT>(a, s);  // 256 x 128 blocks, 8 wavefronts of 64 x 64
+  return launch_tile_cfg<FMT, 2, 2, 4, 4, 1, OUT>(a, s);           // 128 x 128 blocks, 4 wavefronts of 64 x 64
 }
 
 }  // namespace
