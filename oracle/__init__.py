@@ -30,10 +30,13 @@ Modules:
   prose definition, for bit-exact comparison of packed buffers.
 * ``ref``    -- fp64 scaled GEMM, SwiGLU MLP, RMSNorm, decode stack, output
   head, error metrics.
+* ``attention`` -- paged decode attention over an MXFP8 K/V cache with GQA
+  (fish.audio blog, section "Qué hay en código abierto"), and the paged
+  cache layout.
 
 Parity notes: every function is pinned by tests under ``tests/`` against
 closed forms, invariants, brute force or an independent library
 implementation; see each module's header.
 """
 
-from . import fp8, quant, layout, ref  # noqa: F401
+from . import fp8, quant, layout, ref, attention  # noqa: F401
