@@ -379,6 +379,61 @@ def bench_large(torch, sgd, dev):
     return out
 
 
+def bench_attention(torch, sgd, dev, steps):
+    """Paged decode attention over an MXFP8 K/V cache, HBM-bound: batch 64,
+    32 query heads over 8 KV heads of head_dim 128 (the decode stack's
+    d = 2560 model), sequence lengths uniform on [256, 4096], pages shuffled.
+    Bytes per call = the K and V codes and scales of every sequence's tokens
+    + bf16 q and out.  Timed with HIP events over graph replays of R calls
+    over R cache copies (so each call reads its cache cold)."""
+    import numpy as np
+    import synth
+    B, Hq, Hkv, lo, hi = 64, 32, 8, 256, 4096
+    inp = synth.attention_inputs(B, Hq, Hkv, lo, hi, 2400)
+    n_pages = inp["n_pages"]
+    lens = inp["lens"]
+    slots = np.concatenate([inp["pages"][b, np.arange(T) // 16] * 16 + np.arange(T) % 16
+                            for b, T in enumerate(lens)]).astype(np.int32)
+    cache_bytes = sgd.lib().sgd_kv_cache_bytes(n_pages, Hkv)
+    R = max(2, int(np.ceil(1.1e9 / (2 * cache_bytes))))
+    st = torch.from_numpy(slots).to(dev)
+    k0 = sgd.kv_cache_alloc(n_pages, Hkv, dev)
+    v0 = sgd.kv_cache_alloc(n_pages, Hkv, dev)
+    off = 0
+    for b, T in enumerate(lens):
+        sl = st[off:off + T]
+        sgd.kv_cache_write("k", inp["k"][b, :T].contiguous().to(dev), sl, k0, n_pages)
+        sgd.kv_cache_write("v", inp["v"][b, :T].contiguous().to(dev), sl, v0, n_pages)
+        off += T
+    kcs, vcs = [k0] + [k0.clone() for _ in range(R - 1)], [v0] + [v0.clone() for _ in range(R - 1)]
+    q = inp["q"].to(dev)
+    pages = torch.from_numpy(inp["pages"]).to(dev)
+    lt = torch.from_numpy(lens).to(dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    ws = sgd.Workspace(dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        sgd.paged_decode_attention(q, k0, v0, n_pages, pages, lt, Hkv, out=out, workspace=ws)
+        stream.synchronize()
+        g = capture(torch, stream, [lambda r=r: sgd.paged_decode_attention(q, kcs[r], vcs[r], n_pages, pages, lt,
+                                                                             Hkv, out=out, workspace=ws)
+                                    for r in range(R)])
+        reps = time_replays(torch, stream, g, steps, 3, R)
+        del g
+    us = sum(reps) / len(reps)
+    tokens = int(lens.sum())
+    nbytes = tokens * Hkv * 2 * (128 + 4) + 2 * B * Hq * 128 * 2
+    del kcs, vcs, k0, v0
+    torch.cuda.empty_cache()
+    return dict(workload=f"paged decode attention, MXFP8 K/V cache (16-slot pages), B={B}, Hq={Hq}, Hkv={Hkv}, "
+                         f"head_dim 128, lengths uniform {lo}..{hi} (mean {tokens / B:.0f})",
+                us_per_call=round(us, 2), p10_p50_p90=[pct(reps, 10), pct(reps, 50), pct(reps, 90)],
+                algorithmic_bytes=nbytes, gbs=round(nbytes / us / 1e3, 1),
+                roofline=dict(bound="hbm", achieved=round(nbytes / us / 1e3, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)),
+                cache_copies_rotated=R)
+
+
 def cpu_baseline(inp, ms, fmt, y_out, budget_s=10.0):
     """Time the CPU oracle (as it stands) on a bounded sample: passes of one
     MLP call at M=1 and one at M=16 on the headline workload, repeated until
@@ -460,6 +515,8 @@ def main():
                     help="skip the plain streaming-read measurement (profiling runs of the fused kernel)")
     ap.add_argument("--only-main", action="store_true",
                     help="time the headline workload only (no per_config, unfused or warm figures): profiling runs")
+    ap.add_argument("--attention", action="store_true",
+                    help="only the paged decode attention (MXFP8 K/V cache)")
     ap.add_argument("--large", action="store_true",
                     help="only the large-M path (square scaled GEMMs, prefill MLP)")
     ap.add_argument("--stack", action="store_true",
@@ -511,6 +568,9 @@ def main():
         return
     if args.large:
         print(json.dumps(bench_large(torch, sgd, dev)))
+        return
+    if args.attention:
+        print(json.dumps(bench_attention(torch, sgd, dev, args.steps)))
         return
 
     ms = [int(m) for m in args.ms.split(",")]
@@ -564,6 +624,7 @@ def main():
         torch.cuda.empty_cache()
         per_config["decode_stack_d2560_ffn9728_m64"] = bench_stack(torch, sgd, dev, args.steps, args.warmup)
         per_config["large_m"] = bench_large(torch, sgd, dev)
+        per_config["paged_decode_attention"] = bench_attention(torch, sgd, dev, args.steps)
 
     ceiling = None if args.no_read_ceiling else read_ceiling(dev)
 

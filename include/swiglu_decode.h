@@ -329,6 +329,56 @@ int sgd_swiglu_mlp_prefill(const uint16_t* x_bf16, int M, const sgd_weight* gate
                            const sgd_weight* down, uint16_t* y_bf16, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* ---- paged decode attention over an MXFP8 K/V cache -------------------- */
+/*
+ * The other half of a decode step (fish.audio blog, section "Qué hay en
+ * código abierto": MXFP8 FlashAttention, paged decode with native GQA through
+ * a stride-0 K/V broadcast; section "Resultados de benchmark del kernel" for
+ * its measurement).  head_dim is 128.
+ *
+ * Cache: pages of 16 token slots; per (page, KV head) 2112 bytes, so a cache
+ * is [n_pages][Hkv][2112] bytes (16-byte aligned).  Each token's K and V
+ * vectors are quantized on their own in 1x32 MX blocks along head_dim (E4M3,
+ * E8M0 scale) when written.
+ *   K: bytes 0..2047: the 16 x 128 operand tile of the slots (lane l = r + 16q
+ *      holds slot r, dims 16q..16q+15 at bytes 16l.. and dims 64+16q..
+ *      at 1024 + 16l..); bytes 2048 + l: scale of (slot l % 16, block l / 16).
+ *   V: byte 32i + 2r + e: code of (slot r, dim 2i + e), i < 64; bytes
+ *      2048 + 16b + r: scale of (slot r, block b).
+ * Slot s of a sequence's token t is page block_table[b][t / 16], slot t % 16.
+ */
+
+/* Bytes of one cache (K or V): n_pages * Hkv * 2112, or 0 when that reaches 2^31. */
+size_t sgd_kv_cache_bytes(int n_pages, int Hkv);
+
+/* Quantize and write n tokens' vectors x [n, Hkv, head_dim] bf16 into a cache
+ * (kind 0: K layout, 1: V layout) at slots[i] = page * 16 + offset (int32).
+ * Slots outside [0, n_pages * 16) are skipped.  head_dim must be 128.
+ * Errors: SGD_EINVAL, SGD_EDIM, SGD_EALIGN. */
+int sgd_kv_cache_write(int kind, const uint16_t* x_bf16, const int32_t* slots, int n, int Hkv,
+                       int head_dim, uint8_t* cache, int n_pages, void* stream);
+
+/* Workspace of sgd_paged_decode_attention (per-split partial results), or 0
+ * for unsupported sizes. */
+size_t sgd_paged_attention_workspace_bytes(int B, int Hq, int Hkv, int max_pages);
+
+/* out [B, Hq, 128] bf16 = softmax(sm_scale * q' K'^T) V' per sequence b and
+ * query head h over the sequence's seq_lens[b] tokens, q' the query quantized
+ * like the cache (MX, 32-dim blocks), query head h reading KV head
+ * h / (Hq / Hkv) (Hq a multiple of Hkv, at most 16 query heads per KV head).
+ * block_table [B, max_pages] int32 gives each sequence's physical pages;
+ * lengths are clamped to [0, max_pages * 16], a length of 0 gives zeros, and
+ * table entries outside [0, n_pages) read zeros (their values are then
+ * undefined, never an access out of bounds).  Two launches (page splits in
+ * parallel, then their merge).  Errors: SGD_EINVAL, SGD_EDIM (head_dim !=
+ * 128), SGD_EALIGN (q, caches, out 16-byte; table, lengths 4-byte),
+ * SGD_EWORKSPACE. */
+int sgd_paged_decode_attention(const uint16_t* q_bf16, const uint8_t* k_cache,
+                               const uint8_t* v_cache, int n_pages, const int32_t* block_table,
+                               int max_pages, const int32_t* seq_lens, int B, int Hq, int Hkv,
+                               int head_dim, float sm_scale, uint16_t* out_bf16, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /* ---- the unfused pipeline (three launches, intermediates in HBM) -------- */
 /*
  * The same MLP as sgd_fused_swiglu_mlp in three launches whose intermediates

@@ -453,6 +453,72 @@ def swiglu_mlp_prefill(x, gate_up, down, out=None, workspace=None):
     return out
 
 
+HEAD_DIM = 128
+PAGE_SLOTS = 16
+_CTRL_BYTES = 256 * 1024
+
+
+def kv_cache_alloc(n_pages, Hkv, device):
+    """A zeroed paged K or V cache: [n_pages * Hkv * 2112] uint8."""
+    nbytes = lib().sgd_kv_cache_bytes(n_pages, Hkv)
+    if nbytes == 0:
+        raise ValueError(f"unsupported cache size n_pages={n_pages} Hkv={Hkv}")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def kv_cache_write(kind, x, slots, cache, n_pages):
+    """Quantize x [n, Hkv, 128] bf16 and write it into `cache` (kind "k" or
+    "v") at int32 slots [n] (page * 16 + offset)."""
+    if x.dim() != 3 or x.shape[2] != HEAD_DIM:
+        raise ValueError("x must be [n, Hkv, 128]")
+    _need(x, "x", torch.bfloat16)
+    _need(slots, "slots", torch.int32, (x.shape[0],), x.device)
+    _need(cache, "cache", torch.uint8, device=x.device)
+    n, Hkv, _ = x.shape
+    if cache.numel() < lib().sgd_kv_cache_bytes(n_pages, Hkv):
+        raise ValueError("cache too small for n_pages")
+    _lib.check("sgd_kv_cache_write", lib().sgd_kv_cache_write(
+        {"k": 0, "v": 1}[kind], _ptr(x), _ptr(slots), n, Hkv, HEAD_DIM, _ptr(cache), n_pages, _stream(x)))
+    return cache
+
+
+def paged_decode_attention(q, k_cache, v_cache, n_pages, block_table, seq_lens, Hkv, sm_scale=None, out=None,
+                           workspace=None):
+    """out [B, Hq, 128] bf16: decode attention of q [B, Hq, 128] bf16 over the
+    paged MXFP8 caches (block_table [B, max_pages] int32, seq_lens [B]
+    int32), query head h reading KV head h // (Hq // Hkv)."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [B, Hq, 128]")
+    _need(q, "q", torch.bfloat16)
+    B, Hq, _ = q.shape
+    _need(block_table, "block_table", torch.int32, device=q.device)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    max_pages = block_table.shape[1]
+    _need(seq_lens, "seq_lens", torch.int32, (B,), q.device)
+    _need(k_cache, "k_cache", torch.uint8, device=q.device)
+    _need(v_cache, "v_cache", torch.uint8, device=q.device)
+    if sm_scale is None:
+        sm_scale = HEAD_DIM ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, Hq, HEAD_DIM), q.device)
+    need = lib().sgd_paged_attention_workspace_bytes(B, Hq, Hkv, max_pages)
+    if need == 0:
+        raise ValueError(f"unsupported attention sizes B={B} Hq={Hq} Hkv={Hkv} max_pages={max_pages}")
+
+    def launch():
+        # (past the first 256 KB: a shared workspace keeps the persistent
+        # kernels' control block there)
+        ws = _workspace(q.device, need + _CTRL_BYTES, workspace)
+        _lib.check("sgd_paged_decode_attention", lib().sgd_paged_decode_attention(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), n_pages, _ptr(block_table), max_pages, _ptr(seq_lens), B, Hq,
+            Hkv, HEAD_DIM, float(sm_scale), _ptr(out), ctypes.c_void_p(ws.data_ptr() + _CTRL_BYTES),
+            ws.numel() - _CTRL_BYTES, _stream(q)))
+    _serialise_persistent(q.device, launch)
+    return out
+
+
 def fused_swiglu_mlp_noalloc(x, gate, up, down, out):
     """The fused MLP through the entry point that allocates nothing (its
     workspace is the library's fixed per-device array): y [M, d] bf16 into

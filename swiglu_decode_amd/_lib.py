@@ -54,6 +54,10 @@ SIGNATURES = {
     "sgd_scaled_gemm_large": (_i, [_vp, _i, _wp, _vp, _vp, _sz, _vp]),
     "sgd_mlp_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "sgd_swiglu_mlp_prefill": (_i, [_vp, _i, _wp, _wp, _vp, _vp, _sz, _vp]),
+    "sgd_kv_cache_bytes": (_sz, [_i, _i]),
+    "sgd_kv_cache_write": (_i, [_i, _vp, _vp, _i, _i, _i, _vp, _i, _vp]),
+    "sgd_paged_attention_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "sgd_paged_decode_attention": (_i, [_vp, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp, _vp, _sz, _vp]),
     "sgd_scaled_gemm_f32": (_i, [_vp, _i, _wp, _vp, _vp, _sz, _vp]),
     "sgd_act_scales_bytes": (_sz, [_i, _i, _i]),
     "sgd_swiglu_quantize": (_i, [_i, _vp, _i, _i, _vp, _vp, _vp]),

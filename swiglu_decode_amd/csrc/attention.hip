@@ -1,0 +1,398 @@
+// Paged decode attention over an MXFP8 K/V cache with grouped query heads:
+// the other half of a decode step next to the MLP.  fish.audio blog "Cómo
+// hicimos que nuestra API de texto a voz sea gratuita…", section "Qué hay en
+// código abierto": an MXFP8 FlashAttention whose modes include paged decode
+// with native GQA through a stride-0 K/V broadcast (the query heads of a
+// group read their group's K/V once, nothing is replicated per head).
+//
+// Cache.  Each token's K and V vectors (head_dim 128, per KV head) are
+// quantized on their own in 1x32 MX blocks along head_dim when written.
+// Pages hold 16 token slots; per (page, KV head) 2112 bytes:
+//   K: a 16 x 128 tile in the operand order of the scaled fp8 matrix
+//      instruction (lane l = r + 16q: slot r, dims 16q.. and 64+16q..), then
+//      64 scale bytes, byte l = (slot l % 16, block l / 16): the instruction's
+//      scale operand, one byte per lane;
+//   V: byte 32i + 2r + e = (slot r, dim 2i + e), so lane i reads its two dims
+//      of all 16 slots as 32 contiguous bytes; then byte 16b + r = the scale
+//      of (slot r, block b).
+//
+// Decode.  A workgroup takes one (sequence, KV head) and one of S splits of
+// the sequence's pages; its four wavefronts take every fourth page of the
+// split.  Per page: one 16x16x128 MX-scaled fp8 product gives the scores of
+// all (up to 16) query heads of the group against the page's 16 slots, the
+// K tile being the shared operand (the stride-0 broadcast); an online
+// softmax in fp32 (exp2, scores pre-multiplied by sm_scale * log2 e); then
+// o += p V on the vector units, V widened exactly from E4M3 with its scale.
+// The four wavefronts' states are merged in LDS into the split's partial
+// (row max, row sum, unnormalized o); a second kernel merges the splits and
+// writes bf16.  The work is HBM-bound: one pass over the sequence's K and V.
+#include "sgd_act.hpp"
+#include "sgd_device.hpp"
+#include "sgd_host.hpp"
+
+namespace sgd {
+
+namespace {
+
+constexpr int HD = 128;               // head_dim
+constexpr int PSLOTS = 16;            // token slots per page
+constexpr int PAGE_BYTES = 2112;      // per (page, KV head)
+constexpr int MAXG = 16;              // query heads per KV head
+constexpr int RING = 4;               // pages in flight per wavefront
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint16_t* q;   // [B, Hq, 128] bf16
+  const uint8_t* kc;   // [n_pages, Hkv, 2112]
+  const uint8_t* vc;
+  const int32_t* bt;   // [B, max_pages]
+  const int32_t* lens; // [B]
+  int B, Hq, Hkv, G, max_pages, n_pages, S, chunk;  // chunk: pages per split
+  float qk_scale;      // sm_scale * log2(e)
+  float* part;         // [B * Hkv * S][G][2 + 128]: row max (log2 units), row sum, o
+  uint16_t* out;       // [B, Hq, 128] bf16
+};
+
+__device__ __forceinline__ float e8m0_value(uint32_t b) { return pow2_pos((int)(b & 0xFFu) - 127); }
+
+// ---------------------------------------------------------------------------
+// cache write: one lane per (token, KV head, 32-dim block)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kv_write_kernel(int kind, const uint16_t* __restrict__ x,
+                                                       const int32_t* __restrict__ slots, int n, int Hkv,
+                                                       uint8_t* __restrict__ cache, int n_pages) {
+  const long long lane_all = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long vec = lane_all >> 2;
+  const int j = (int)(lane_all & 3);
+  if (vec >= (long long)n * Hkv) return;  // (whole groups of four lanes: vec is shared by them)
+  const int t = (int)(vec / Hkv), h = (int)(vec - (long long)t * Hkv);
+  const int slot = slots[t];
+  const bool ok = slot >= 0 && slot < n_pages * PSLOTS;  // (invalid slots are skipped)
+  float v[32];
+  const uint4* src = reinterpret_cast<const uint4*>(x + vec * HD + 32 * j);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 w = src[c];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * c + 2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
+      v[8 * c + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+    }
+  }
+  uint32_t cw[8], se = 0;
+  float sf = 1.0f;
+  quant_block32<FMT_MX>(v, cw, &sf, &se);
+  if (!ok) return;
+  const int page = slot / PSLOTS, r = slot - page * PSLOTS;
+  uint8_t* base = cache + ((size_t)page * Hkv + h) * PAGE_BYTES;
+  if (kind == 0) {
+    // dims 32j..32j+31 are 16-dim segments 2j and 2j+1; segment s sits at
+    // half s / 4, lane r + 16 (s % 4)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int s = 2 * j + u;
+      *reinterpret_cast<uint4*>(base + (s >> 2) * 1024 + (r + 16 * (s & 3)) * 16) =
+          make_uint4(cw[4 * u], cw[4 * u + 1], cw[4 * u + 2], cw[4 * u + 3]);
+    }
+    base[2048 + r + 16 * j] = (uint8_t)se;
+  } else {
+    // dim pair i = 16j + k: bytes 32i + 2r, 32i + 2r + 1
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t pair = (cw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+      *reinterpret_cast<uint16_t*>(base + 32 * (16 * j + k) + 2 * r) = (uint16_t)pair;
+    }
+    base[2048 + 16 * j + r] = (uint8_t)se;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode: one workgroup per (sequence, KV head, split), four wavefronts
+// ---------------------------------------------------------------------------
+struct AttnLds {
+  uint8_t qt[2048];           // the group's quantized queries as the A operand tile (rows >= G zero)
+  uint8_t qs[64];             // their scale bytes, byte l = (head l % 16, block l / 16)
+  float p[4][MAXG][PSLOTS];   // per wavefront: probabilities of the current page
+  float alpha[4][MAXG];       // per wavefront: rescale factors of the current page
+  float m[4][MAXG], l[4][MAXG];
+  float o[4][MAXG][HD];
+};
+
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
+  __shared__ AttnLds L;
+  const int l = lane_id(), wv = (int)(threadIdx.x >> 6);
+  const int S = a.S;
+  const int split = blockIdx.x % S, bh = blockIdx.x / S;
+  const int b = bh / a.Hkv, kvh = bh - b * a.Hkv;
+  const int G = a.G;
+  int T = a.lens[b];
+  T = T < 0 ? 0 : (T > a.max_pages * PSLOTS ? a.max_pages * PSLOTS : T);
+  const int npages = (T + PSLOTS - 1) / PSLOTS;
+  const int p0 = split * a.chunk, p1 = min(npages, p0 + a.chunk);
+
+  // the group's queries, quantized (MX, 32-dim blocks) into the A tile
+  for (int i = threadIdx.x; i < 2048 / 16; i += 256) reinterpret_cast<uint4*>(L.qt)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x < 64) L.qs[threadIdx.x] = 127u;  // (rows >= G: zero codes, unit scale)
+  __syncthreads();
+  if (wv == 0 && l < 4 * G) {  // (lanes of a head are four consecutive ones, all active)
+    const int g = l >> 2, j = l & 3;
+    const uint4* src = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + (size_t)kvh * G + g) * HD + 32 * j);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 w = src[c];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * c + 2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
+        v[8 * c + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+      }
+    }
+    uint32_t cw[8], se = 0;
+    float sf = 1.0f;
+    quant_block32<FMT_MX>(v, cw, &sf, &se);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int s = 2 * j + u;
+      *reinterpret_cast<uint4*>(L.qt + (s >> 2) * 1024 + (g + 16 * (s & 3)) * 16) =
+          make_uint4(cw[4 * u], cw[4 * u + 1], cw[4 * u + 2], cw[4 * u + 3]);
+    }
+    L.qs[g + 16 * j] = (uint8_t)se;
+  }
+  __syncthreads();
+  const v8i qa = make_v8i(*reinterpret_cast<const uint4*>(L.qt + l * 16),
+                          *reinterpret_cast<const uint4*>(L.qt + 1024 + l * 16));
+  const int qsc = L.qs[l];
+
+  // this wavefront's state: per head (row 4(l/16) + rr of the scores, held
+  // alike by the 16 lanes of a row group) the running max and sum; per lane
+  // o of dims 2l, 2l+1 for every head
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    mrow[rr] = -INFINITY;
+    lrow[rr] = 0.0f;
+  }
+  float o[MAXG][2];
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) o[g][0] = o[g][1] = 0.0f;
+
+  const uint32_t cache_bytes = (uint32_t)a.n_pages * (uint32_t)a.Hkv * (uint32_t)PAGE_BYTES;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc, cache_bytes), rv = make_rsrc(a.vc, cache_bytes);
+  const int32_t* bt = a.bt + (size_t)b * a.max_pages;
+  struct Slot {
+    v8i k;
+    uint32_t ks;
+    uint4 v0, v1;
+    uint4 vs;
+  } R[RING];
+  // this wavefront's pages are p0 + wv + 4k; lane i holds the physical page
+  // of k = 64 * idblk + i, reloaded every 64 pages
+  int idblk = -1, ids = 0;
+  auto issue = [&](int u, int p) {
+    uint32_t base = 0x80000000u;  // (past the cache: reads zero)
+    if (p < p1) {
+      const int k = (p - p0 - wv) >> 2;
+      if ((k >> 6) != idblk) {
+        idblk = k >> 6;
+        const int pi = p0 + wv + 4 * (64 * idblk + l);
+        ids = pi < p1 ? bt[pi] : -1;
+      }
+      const int phys = __builtin_amdgcn_readlane(ids, k & 63);
+      if (phys >= 0 && phys < a.n_pages) base = ((uint32_t)phys * (uint32_t)a.Hkv + (uint32_t)kvh) * PAGE_BYTES;
+    }
+    const bool in = base != 0x80000000u;
+    R[u].k = make_v8i(__builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, in ? base + l * 16 : base, 0, AUX_NT)),
+                      __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, in ? base + 1024 + l * 16 : base, 0, AUX_NT)));
+    R[u].ks = __builtin_amdgcn_raw_buffer_load_b8(rk, in ? base + 2048 + l : base, 0, 0);
+    R[u].v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + l * 32 : base, 0, AUX_NT));
+    R[u].v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + l * 32 + 16 : base, 0, AUX_NT));
+    R[u].vs = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + 2048 + 16 * (l >> 4) : base, 0, 0));
+  };
+  int p = p0 + wv;
+#pragma unroll
+  for (int u = 0; u < RING; ++u) issue(u, p + 4 * u);
+  for (; p < p1; p += 4 * RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      const int pg = p + 4 * u;
+      if (pg < p1) {
+        // scores of heads 4(l/16)+rr against slot l%16, in log2 units
+        const v4f z = {0.f, 0.f, 0.f, 0.f};
+        const v4f sc = mfma_f8(qa, R[u].k, z, qsc, (int)R[u].ks);
+        const bool live = pg * PSLOTS + (l & 15) < T;
+        float pr[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float s = live ? sc[rr] * a.qk_scale : -INFINITY;
+          float mx = s;
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, WAVE));
+          const float mn = fmaxf(mrow[rr], mx);  // (finite: slot 0 of a page below p1 is live)
+          const float al = exp2f(mrow[rr] - mn);
+          pr[rr] = live ? exp2f(s - mn) : 0.0f;
+          float sm = pr[rr];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) sm += __shfl_xor(sm, off, WAVE);
+          lrow[rr] = lrow[rr] * al + sm;
+          mrow[rr] = mn;
+          const int g = 4 * (l >> 4) + rr;
+          L.p[wv][g][l & 15] = pr[rr];
+          if ((l & 15) == 0) L.alpha[wv][g] = al;
+        }
+        // (LDS writes and reads of one wavefront complete in program order)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // o = alpha o + p V for dims 2l, 2l+1; V of slot r is zero where not live
+        float v[PSLOTS][2];
+        const uint32_t vw[8] = {R[u].v0.x, R[u].v0.y, R[u].v0.z, R[u].v0.w, R[u].v1.x, R[u].v1.y, R[u].v1.z, R[u].v1.w};
+        const uint32_t vsw[4] = {R[u].vs.x, R[u].vs.y, R[u].vs.z, R[u].vs.w};
+#pragma unroll
+        for (int r = 0; r < PSLOTS; ++r) {
+          const float scl = e8m0_value(vsw[r >> 2] >> (8 * (r & 3)));
+          const auto f = (r & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vw[r >> 1], scl, true)
+                                 : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vw[r >> 1], scl, false);
+          const bool lv = pg * PSLOTS + r < T;
+          v[r][0] = lv ? f[0] : 0.0f;
+          v[r][1] = lv ? f[1] : 0.0f;
+        }
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g) {
+          if (g < G) {
+            const float al = L.alpha[wv][g];
+            float a0 = o[g][0] * al, a1 = o[g][1] * al;
+#pragma unroll
+            for (int r4 = 0; r4 < PSLOTS; r4 += 4) {
+              const v4f pp = *reinterpret_cast<const v4f*>(&L.p[wv][g][r4]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                a0 = fmaf(pp[e], v[r4 + e][0], a0);
+                a1 = fmaf(pp[e], v[r4 + e][1], a1);
+              }
+            }
+            o[g][0] = a0;
+            o[g][1] = a1;
+          }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      }
+      issue(u, pg + 4 * RING);
+    }
+  }
+
+  // merge the four wavefronts into the split's partial
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int g = 4 * (l >> 4) + rr;
+    if ((l & 15) == 0) {
+      L.m[wv][g] = mrow[rr];
+      L.l[wv][g] = lrow[rr];
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g)
+    if (g < G) *reinterpret_cast<float2*>(&L.o[wv][g][2 * l]) = make_float2(o[g][0], o[g][1]);
+  __syncthreads();
+  float* part = a.part + (size_t)blockIdx.x * G * (2 + HD);
+  for (int i = threadIdx.x; i < G * HD; i += 256) {
+    const int g = i / HD, dd = i - g * HD;
+    float M = L.m[0][g];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, L.m[w][g]);
+    float acc = 0.0f, sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = L.m[w][g] == -INFINITY ? 0.0f : exp2f(L.m[w][g] - M);
+      acc += L.o[w][g][dd] * f;
+      sum += L.l[w][g] * f;
+    }
+    part[g * (2 + HD) + 2 + dd] = acc;
+    if (dd == 0) {
+      part[g * (2 + HD)] = M;
+      part[g * (2 + HD) + 1] = sum;
+    }
+  }
+}
+
+// The splits of each (sequence, query head) merged: one wavefront each, two
+// dims per lane.  A sequence of length 0 gives zeros.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const long long wave = ((long long)blockIdx.x * 256 + threadIdx.x) >> 6;
+  if (wave >= (long long)a.B * a.Hq) return;
+  const int l = lane_id();
+  const int b = (int)(wave / a.Hq), h = (int)(wave - (long long)b * a.Hq);
+  const int kvh = h / a.G, g = h - kvh * a.G;
+  const size_t stride = (size_t)a.G * (2 + HD);
+  const float* base = a.part + ((size_t)b * a.Hkv + kvh) * a.S * stride + (size_t)g * (2 + HD);
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmaxf(M, base[s * stride]);
+  float o0 = 0.0f, o1 = 0.0f, sum = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.S; ++s) {
+      const float m = base[s * stride];
+      if (m == -INFINITY) continue;
+      const float f = exp2f(m - M);
+      sum += base[s * stride + 1] * f;
+      o0 += base[s * stride + 2 + 2 * l] * f;
+      o1 += base[s * stride + 2 + 2 * l + 1] * f;
+    }
+  }
+  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+  const uint32_t w = f32_to_bf16(o0 * inv) | (f32_to_bf16(o1 * inv) << 16);
+  reinterpret_cast<uint32_t*>(a.out + ((size_t)b * a.Hq + h) * HD)[l] = w;
+}
+
+int attn_splits(int B, int Hkv, int max_pages) {
+  // enough workgroups to fill the GPU several times over, splits of at least
+  // 8 pages (128 tokens)
+  int s = (2048 + B * Hkv - 1) / (B * Hkv);
+  const int by_len = (max_pages + 7) / 8;
+  if (s > by_len) s = by_len;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int max_pages) {
+  const int S = attn_splits(B, Hkv, max_pages);
+  return (size_t)B * Hkv * S * (size_t)(Hq / Hkv) * (2 + HD) * sizeof(float);
+}
+
+int launch_kv_write(int kind, const uint16_t* x, const int32_t* slots, int n, int Hkv, uint8_t* cache, int n_pages,
+                    hipStream_t s) {
+  const long long lanes = (long long)n * Hkv * 4;
+  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, kind, x, slots, n, Hkv,
+                     cache, n_pages);
+  return hip_status(hipGetLastError());
+}
+
+int launch_paged_decode(const uint16_t* q, const uint8_t* kc, const uint8_t* vc, int n_pages, const int32_t* bt,
+                        int max_pages, const int32_t* lens, int B, int Hq, int Hkv, float sm_scale, uint16_t* out,
+                        void* ws, hipStream_t s) {
+  AttnArgs a{};
+  a.q = q;
+  a.kc = kc;
+  a.vc = vc;
+  a.bt = bt;
+  a.lens = lens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.max_pages = max_pages;
+  a.n_pages = n_pages;
+  a.S = attn_splits(B, Hkv, max_pages);
+  a.chunk = (max_pages + a.S - 1) / a.S;
+  a.qk_scale = sm_scale * LOG2E;
+  a.part = static_cast<float*>(ws);
+  a.out = out;
+  hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)(B * Hkv * a.S)), dim3(256), 0, s, a);
+  int rc = hip_status(hipGetLastError());
+  if (rc) return rc;
+  const long long waves = (long long)B * Hq;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace sgd

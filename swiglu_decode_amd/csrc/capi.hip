@@ -390,6 +390,54 @@ int sgd_swiglu_mlp_prefill(const uint16_t* x_bf16, int M, const sgd_weight* gate
   return launch_tile_gemm(fmt, aq, as, M, F, down, y_bf16, false, s);
 }
 
+// ---- paged decode attention ----
+namespace {
+constexpr int ATTN_HD = 128, ATTN_PAGE_BYTES = 2112;
+bool attn_dims_ok(int B, int Hq, int Hkv, int n_pages, int max_pages) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_pages <= 0 || max_pages <= 0) return false;
+  if (B > 65536 || Hq > 1024 || max_pages > (1 << 20)) return false;
+  if (Hq % Hkv || Hq / Hkv > 16) return false;
+  return (size_t)n_pages * (size_t)Hkv * ATTN_PAGE_BYTES < ((size_t)1 << 31);
+}
+}  // namespace
+
+size_t sgd_kv_cache_bytes(int n_pages, int Hkv) {
+  if (n_pages <= 0 || Hkv <= 0 || (size_t)n_pages * (size_t)Hkv * ATTN_PAGE_BYTES >= ((size_t)1 << 31)) return 0;
+  return (size_t)n_pages * (size_t)Hkv * ATTN_PAGE_BYTES;
+}
+
+int sgd_kv_cache_write(int kind, const uint16_t* x_bf16, const int32_t* slots, int n, int Hkv, int head_dim,
+                       uint8_t* cache, int n_pages, void* stream) {
+  if (kind != 0 && kind != 1) return SGD_EINVAL;
+  if (!x_bf16 || !slots || !cache || n <= 0 || n > (1 << 24) || Hkv <= 0 || Hkv > 1024) return SGD_EINVAL;
+  if (head_dim != ATTN_HD) return SGD_EDIM;
+  if (sgd_kv_cache_bytes(n_pages, Hkv) == 0) return SGD_EINVAL;
+  if (!al16(x_bf16) || !al16(cache) || !al4(slots)) return SGD_EALIGN;
+  return launch_kv_write(kind, x_bf16, slots, n, Hkv, cache, n_pages, as_stream(stream));
+}
+
+size_t sgd_paged_attention_workspace_bytes(int B, int Hq, int Hkv, int max_pages) {
+  if (!attn_dims_ok(B, Hq, Hkv, 1, max_pages)) return 0;
+  return attn_workspace_bytes(B, Hq, Hkv, max_pages);
+}
+
+int sgd_paged_decode_attention(const uint16_t* q_bf16, const uint8_t* k_cache, const uint8_t* v_cache, int n_pages,
+                               const int32_t* block_table, int max_pages, const int32_t* seq_lens, int B, int Hq,
+                               int Hkv, int head_dim, float sm_scale, uint16_t* out_bf16, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  if (!q_bf16 || !k_cache || !v_cache || !block_table || !seq_lens || !out_bf16) return SGD_EINVAL;
+  if (head_dim != ATTN_HD) return SGD_EDIM;
+  if (!attn_dims_ok(B, Hq, Hkv, n_pages, max_pages)) return SGD_EINVAL;
+  if (!(sm_scale > 0.0f) || sm_scale > 1e6f) return SGD_EINVAL;
+  if (!al16(q_bf16) || !al16(k_cache) || !al16(v_cache) || !al16(out_bf16) || !al4(block_table) || !al4(seq_lens))
+    return SGD_EALIGN;
+  if (!workspace) return SGD_EWORKSPACE;
+  if (!al16(workspace)) return SGD_EALIGN;
+  if (ws_bytes < attn_workspace_bytes(B, Hq, Hkv, max_pages)) return SGD_EWORKSPACE;
+  return launch_paged_decode(q_bf16, k_cache, v_cache, n_pages, block_table, max_pages, seq_lens, B, Hq, Hkv, sm_scale,
+                             out_bf16, workspace, as_stream(stream));
+}
+
 int sgd_bf16_to_f32(const uint16_t* x_bf16, int M, int d, float* h, void* stream) {
   if (!x_bf16 || !h || M <= 0 || d <= 0 || M > 65536 || d > MAX_DIM) return SGD_EINVAL;
   if (d % 128) return SGD_EDIM;

@@ -56,6 +56,13 @@ size_t act_tiles_scales_bytes(int fmt, int M, int K);
 int launch_act_tiles(int fmt, const uint16_t* x, int M, int K, uint8_t* codes, void* scales, hipStream_t s);
 int launch_tile_gemm(int fmt, const uint8_t* a, const void* as, int M, int K, const sgd_weight* w, void* c,
                      bool out_f32, hipStream_t s);
+// Paged decode attention over an MXFP8 K/V cache (head_dim 128, 16-slot pages).
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int max_pages);
+int launch_kv_write(int kind, const uint16_t* x, const int32_t* slots, int n, int Hkv, uint8_t* cache, int n_pages,
+                    hipStream_t s);
+int launch_paged_decode(const uint16_t* q, const uint8_t* kc, const uint8_t* vc, int n_pages, const int32_t* bt,
+                        int max_pages, const int32_t* lens, int B, int Hq, int Hkv, float sm_scale, uint16_t* out,
+                        void* ws, hipStream_t s);
 int launch_stream(const Problem& p, hipStream_t s);
 
 // Host-side validation of a fused-MLP call's arguments other than its

@@ -17,6 +17,10 @@ float32, then rounded to bf16 with round-to-nearest-even by torch's CPU cast):
 * decode stack (d=2560, F=9728, 24 layers, M=64): layer l draws its three
   weights from seed 1005 + 100 * l; x from seed 1005 + 9998; the bf16 output
   head [4096, 2560] ~ N(0, 0.02) from seed 1005 + 9999.
+* paged decode attention (head_dim 128): sequence lengths uniform on
+  [lo, hi] (integers), then q [B, Hq, 128], k and v [B, Tmax, Hkv, 128] all
+  N(0, 1), then a random permutation assigning physical 16-slot pages to the
+  sequences' logical pages (in sequence order), from one seed.
 """
 
 from dataclasses import dataclass, field
@@ -123,3 +127,25 @@ def random_bf16(shape, seed, std=1.0):
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> float64 numpy array (exact)."""
     return t.detach().to("cpu").float().numpy().astype(np.float64)
+
+
+def attention_inputs(B, Hq, Hkv, lo, hi, seed, extra_pages=0):
+    """Seeded decode-attention inputs: dict(lens int32 [B], q bf16 [B, Hq, 128],
+    k, v bf16 [B, Tmax, Hkv, 128], pages int32 [B, max_pages] (physical page of
+    each logical page, -1 past a sequence's pages), n_pages)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+    T = int(lens.max())
+    q = to_bf16_tensor(rng.standard_normal((B, Hq, 128)).astype(np.float32))
+    k = to_bf16_tensor(rng.standard_normal((B, T, Hkv, 128)).astype(np.float32))
+    v = to_bf16_tensor(rng.standard_normal((B, T, Hkv, 128)).astype(np.float32))
+    npg = (lens + 15) // 16
+    max_pages = int(npg.max())
+    n_pages = int(npg.sum()) + extra_pages
+    perm = rng.permutation(n_pages).astype(np.int32)
+    pages = np.full((B, max_pages), -1, dtype=np.int32)
+    o = 0
+    for b in range(B):
+        pages[b, :npg[b]] = perm[o:o + npg[b]]
+        o += npg[b]
+    return dict(lens=lens, q=q, k=k, v=v, pages=pages, n_pages=n_pages)

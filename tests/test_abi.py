@@ -141,6 +141,32 @@ def test_argument_errors_launch_nothing(L):
     assert blk(g, u, d, eps=-1.0) == E["EINVAL"]
     assert blk(g, u, d, eps=float("nan")) == E["EINVAL"]
     assert blk(g, u, d, ws=need - 16) == E["EWORKSPACE"]
+    # paged decode attention and its cache writer: argument errors only
+    assert L.sgd_kv_cache_bytes(10, 8) == 10 * 8 * 2112
+    assert L.sgd_kv_cache_bytes(1 << 20, 1024) == 0
+    kw = lambda kind=0, x=0x1000, sl=0x2000, n=4, Hkv=2, hd=128, c=0x3000, npg=8: L.sgd_kv_cache_write(
+        kind, P(x), P(sl), n, Hkv, hd, P(c), npg, None)
+    assert kw(kind=2) == E["EINVAL"]
+    assert kw(hd=64) == E["EDIM"]
+    assert kw(n=0) == E["EINVAL"]
+    assert kw(x=0) == E["EINVAL"]
+    assert kw(x=0x1008) == E["EALIGN"]
+    assert kw(sl=0x2002) == E["EALIGN"]
+    assert L.sgd_paged_attention_workspace_bytes(4, 32, 8, 100) > 0
+    assert L.sgd_paged_attention_workspace_bytes(4, 30, 8, 100) == 0  # Hq not a multiple of Hkv
+    assert L.sgd_paged_attention_workspace_bytes(4, 64, 2, 100) == 0  # 32 query heads per KV head
+    wsa = L.sgd_paged_attention_workspace_bytes(4, 32, 8, 100)
+    pa = lambda q=0x1000, B=4, Hq=32, Hkv=8, hd=128, sc=0.088, ws=wsa, bt=0x4000: L.sgd_paged_decode_attention(
+        P(q), P(0x2000), P(0x3000), 50, P(bt), 100, P(0x5000), B, Hq, Hkv, hd, ctypes.c_float(sc), P(0x6000),
+        P(0x7000), ws, None)
+    assert pa(hd=64) == E["EDIM"]
+    assert pa(Hq=30) == E["EINVAL"]
+    assert pa(B=0) == E["EINVAL"]
+    assert pa(sc=0.0) == E["EINVAL"]
+    assert pa(sc=float("nan")) == E["EINVAL"]
+    assert pa(q=0x1008) == E["EALIGN"]
+    assert pa(bt=0x4002) == E["EALIGN"]
+    assert pa(ws=wsa - 4) == E["EWORKSPACE"]
     # workspace status query: argument errors only (no GPU here)
     assert L.sgd_workspace_status(None, None) == E["EINVAL"]
     assert L.sgd_workspace_status(P(0x1004), None) == E["EALIGN"]
