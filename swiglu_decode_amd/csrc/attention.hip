@@ -18,11 +18,12 @@
 //
 // Decode.  A workgroup takes one (sequence, KV head) and one of S splits of
 // the sequence's pages; its four wavefronts take every fourth page of the
-// split.  Per page: one 16x16x128 MX-scaled fp8 product gives the scores of
-// all (up to 16) query heads of the group against the page's 16 slots, the
-// K tile being the shared operand (the stride-0 broadcast); an online
-// softmax in fp32 (exp2, scores pre-multiplied by sm_scale * log2 e); then
-// o += p V on the vector units, V widened exactly from E4M3 with its scale.
+// split, RING pages in flight each.  Per page one 16x16x128 MX-scaled fp8
+// product gives the scores of all (up to 16) query heads of the group
+// against the page's 16 slots, the K tile being the shared operand (the
+// stride-0 broadcast); the online softmax (fp32, exp2, scores pre-multiplied
+// by sm_scale * log2 e) is updated once per RING pages; then o += p V on the
+// vector units, V widened exactly from E4M3 with its scale.
 // The four wavefronts' states are merged in LDS into the split's partial
 // (row max, row sum, unnormalized o); a second kernel merges the splits and
 // writes bf16.  The work is HBM-bound: one pass over the sequence's K and V.
@@ -38,7 +39,8 @@ constexpr int HD = 128;               // head_dim
 constexpr int PSLOTS = 16;            // token slots per page
 constexpr int PAGE_BYTES = 2112;      // per (page, KV head)
 constexpr int MAXG = 16;              // query heads per KV head
-constexpr int RING = 4;               // pages in flight per wavefront
+constexpr int RING = 2;               // pages in flight per wavefront (4 and 8 measured slower: fewer wavefronts fit)
+constexpr int MAXCHUNK = 1024;        // pages of one split (their ids are staged in LDS)
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -54,6 +56,28 @@ struct AttnArgs {
 };
 
 __device__ __forceinline__ float e8m0_value(uint32_t b) { return pow2_pos((int)(b & 0xFFu) - 127); }
+
+// Max / sum over each row of 16 lanes, every lane of the row receiving the
+// result: lane exchanges within quads (swap neighbours, then pairs), then
+// the half-row and row mirrors (lane i with 7-i, then with 15-i), all
+// register moves between lanes (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  return fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<DPP_QUAD_XOR1>(v);
+  v += dpp<DPP_QUAD_XOR2>(v);
+  v += dpp<DPP_ROW_HALF_MIRROR>(v);
+  return v + dpp<DPP_ROW_MIRROR>(v);
+}
 
 // ---------------------------------------------------------------------------
 // cache write: one lane per (token, KV head, 32-dim block)
@@ -113,12 +137,14 @@ __global__ __launch_bounds__(256) void kv_write_kernel(int kind, const uint16_t*
 struct AttnLds {
   uint8_t qt[2048];           // the group's quantized queries as the A operand tile (rows >= G zero)
   uint8_t qs[64];             // their scale bytes, byte l = (head l % 16, block l / 16)
-  float p[4][MAXG][PSLOTS];   // per wavefront: probabilities of the current page
-  float alpha[4][MAXG];       // per wavefront: rescale factors of the current page
+  float p[4][MAXG][RING * PSLOTS];  // per wavefront: probabilities of the step's pages
+  float alpha[4][MAXG];       // per wavefront: rescale factors of the step
   float m[4][MAXG], l[4][MAXG];
   float o[4][MAXG][HD];
+  int ids[MAXCHUNK];          // physical pages of this split
 };
 
+template <int NG>  // query heads per KV head, rounded up to a power of two (<= 16)
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   __shared__ AttnLds L;
   const int l = lane_id(), wv = (int)(threadIdx.x >> 6);
@@ -134,6 +160,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   // the group's queries, quantized (MX, 32-dim blocks) into the A tile
   for (int i = threadIdx.x; i < 2048 / 16; i += 256) reinterpret_cast<uint4*>(L.qt)[i] = make_uint4(0u, 0u, 0u, 0u);
   if (threadIdx.x < 64) L.qs[threadIdx.x] = 127u;  // (rows >= G: zero codes, unit scale)
+  // the split's page ids, staged once (so that no load of the page loop
+  // depends on another load)
+  for (int i = p0 + (int)threadIdx.x; i < p1; i += 256) L.ids[i - p0] = a.bt[(size_t)b * a.max_pages + i];
   __syncthreads();
   if (wv == 0 && l < 4 * G) {  // (lanes of a head are four consecutive ones, all active)
     const int g = l >> 2, j = l & 3;
@@ -174,32 +203,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     mrow[rr] = -INFINITY;
     lrow[rr] = 0.0f;
   }
-  float o[MAXG][2];
+  float o[NG][2];
 #pragma unroll
-  for (int g = 0; g < MAXG; ++g) o[g][0] = o[g][1] = 0.0f;
+  for (int g = 0; g < NG; ++g) o[g][0] = o[g][1] = 0.0f;
 
   const uint32_t cache_bytes = (uint32_t)a.n_pages * (uint32_t)a.Hkv * (uint32_t)PAGE_BYTES;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc, cache_bytes), rv = make_rsrc(a.vc, cache_bytes);
-  const int32_t* bt = a.bt + (size_t)b * a.max_pages;
   struct Slot {
     v8i k;
     uint32_t ks;
     uint4 v0, v1;
     uint4 vs;
   } R[RING];
-  // this wavefront's pages are p0 + wv + 4k; lane i holds the physical page
-  // of k = 64 * idblk + i, reloaded every 64 pages
-  int idblk = -1, ids = 0;
   auto issue = [&](int u, int p) {
     uint32_t base = 0x80000000u;  // (past the cache: reads zero)
     if (p < p1) {
-      const int k = (p - p0 - wv) >> 2;
-      if ((k >> 6) != idblk) {
-        idblk = k >> 6;
-        const int pi = p0 + wv + 4 * (64 * idblk + l);
-        ids = pi < p1 ? bt[pi] : -1;
-      }
-      const int phys = __builtin_amdgcn_readlane(ids, k & 63);
+      const int phys = L.ids[p - p0];
       if (phys >= 0 && phys < a.n_pages) base = ((uint32_t)phys * (uint32_t)a.Hkv + (uint32_t)kvh) * PAGE_BYTES;
     }
     const bool in = base != 0x80000000u;
@@ -214,56 +233,74 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < RING; ++u) issue(u, p + 4 * u);
   for (; p < p1; p += 4 * RING) {
+    // the scores of the step's RING pages (heads 4(l/16)+rr against slot
+    // l%16 of page u, in log2 units), then one online-softmax update for all
+    // of them
+    v4f sc[RING];
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+      sc[u] = p + 4 * u < p1 ? mfma_f8(qa, R[u].k, z, qsc, (int)R[u].ks) : z;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float sv[RING], mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < RING; ++u) {
+        const bool live = p + 4 * u < p1 && (p + 4 * u) * PSLOTS + (l & 15) < T;  // (this split's pages only)
+        sv[u] = live ? sc[u][rr] * a.qk_scale : -INFINITY;
+        mx = fmaxf(mx, sv[u]);
+      }
+      mx = row16_max(mx);
+      const float mn = fmaxf(mrow[rr], mx);  // (finite: slot 0 of page p is live)
+      const float al = exp2f(mrow[rr] - mn);
+      float sm = 0.0f;
+      const int g = 4 * (l >> 4) + rr;
+#pragma unroll
+      for (int u = 0; u < RING; ++u) {
+        const float pr = sv[u] == -INFINITY ? 0.0f : exp2f(sv[u] - mn);
+        sm += pr;
+        L.p[wv][g][u * PSLOTS + (l & 15)] = pr;
+      }
+      lrow[rr] = lrow[rr] * al + row16_sum(sm);
+      mrow[rr] = mn;
+      if ((l & 15) == 0) L.alpha[wv][g] = al;
+    }
+    // (LDS writes and reads of one wavefront complete in program order)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      if (g < G) {
+        const float al = L.alpha[wv][g];
+        o[g][0] *= al;
+        o[g][1] *= al;
+      }
+    // o += p V page by page (dims 2l, 2l+1; V of slots past the length is
+    // zero), each page's loads reissued for the next step once used
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
       const int pg = p + 4 * u;
       if (pg < p1) {
-        // scores of heads 4(l/16)+rr against slot l%16, in log2 units
-        const v4f z = {0.f, 0.f, 0.f, 0.f};
-        const v4f sc = mfma_f8(qa, R[u].k, z, qsc, (int)R[u].ks);
-        const bool live = pg * PSLOTS + (l & 15) < T;
-        float pr[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float s = live ? sc[rr] * a.qk_scale : -INFINITY;
-          float mx = s;
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, WAVE));
-          const float mn = fmaxf(mrow[rr], mx);  // (finite: slot 0 of a page below p1 is live)
-          const float al = exp2f(mrow[rr] - mn);
-          pr[rr] = live ? exp2f(s - mn) : 0.0f;
-          float sm = pr[rr];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) sm += __shfl_xor(sm, off, WAVE);
-          lrow[rr] = lrow[rr] * al + sm;
-          mrow[rr] = mn;
-          const int g = 4 * (l >> 4) + rr;
-          L.p[wv][g][l & 15] = pr[rr];
-          if ((l & 15) == 0) L.alpha[wv][g] = al;
-        }
-        // (LDS writes and reads of one wavefront complete in program order)
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        // o = alpha o + p V for dims 2l, 2l+1; V of slot r is zero where not live
         float v[PSLOTS][2];
         const uint32_t vw[8] = {R[u].v0.x, R[u].v0.y, R[u].v0.z, R[u].v0.w, R[u].v1.x, R[u].v1.y, R[u].v1.z, R[u].v1.w};
         const uint32_t vsw[4] = {R[u].vs.x, R[u].vs.y, R[u].vs.z, R[u].vs.w};
+        const bool full = (pg + 1) * PSLOTS <= T;
 #pragma unroll
         for (int r = 0; r < PSLOTS; ++r) {
           const float scl = e8m0_value(vsw[r >> 2] >> (8 * (r & 3)));
           const auto f = (r & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vw[r >> 1], scl, true)
                                  : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vw[r >> 1], scl, false);
-          const bool lv = pg * PSLOTS + r < T;
+          const bool lv = full || pg * PSLOTS + r < T;
           v[r][0] = lv ? f[0] : 0.0f;
           v[r][1] = lv ? f[1] : 0.0f;
         }
 #pragma unroll
-        for (int g = 0; g < MAXG; ++g) {
+        for (int g = 0; g < NG; ++g) {
           if (g < G) {
-            const float al = L.alpha[wv][g];
-            float a0 = o[g][0] * al, a1 = o[g][1] * al;
+            float a0 = o[g][0], a1 = o[g][1];
 #pragma unroll
             for (int r4 = 0; r4 < PSLOTS; r4 += 4) {
-              const v4f pp = *reinterpret_cast<const v4f*>(&L.p[wv][g][r4]);
+              const v4f pp = *reinterpret_cast<const v4f*>(&L.p[wv][g][u * PSLOTS + r4]);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 a0 = fmaf(pp[e], v[r4 + e][0], a0);
@@ -274,10 +311,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
             o[g][1] = a1;
           }
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
       }
       issue(u, pg + 4 * RING);
     }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
 
   // merge the four wavefronts into the split's partial
@@ -290,7 +327,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     }
   }
 #pragma unroll
-  for (int g = 0; g < MAXG; ++g)
+  for (int g = 0; g < NG; ++g)
     if (g < G) *reinterpret_cast<float2*>(&L.o[wv][g][2 * l]) = make_float2(o[g][0], o[g][1]);
   __syncthreads();
   float* part = a.part + (size_t)blockIdx.x * G * (2 + HD);
@@ -344,11 +381,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 int attn_splits(int B, int Hkv, int max_pages) {
   // enough workgroups to fill the GPU several times over, splits of at least
-  // 8 pages (128 tokens)
+  // 8 pages (128 tokens) and at most MAXCHUNK
   int s = (2048 + B * Hkv - 1) / (B * Hkv);
   const int by_len = (max_pages + 7) / 8;
   if (s > by_len) s = by_len;
   if (s > 64) s = 64;
+  const int need = (max_pages + MAXCHUNK - 1) / MAXCHUNK;
+  if (s < need) s = need;
   return s < 1 ? 1 : s;
 }
 
@@ -387,7 +426,17 @@ int launch_paged_decode(const uint16_t* q, const uint8_t* kc, const uint8_t* vc,
   a.qk_scale = sm_scale * LOG2E;
   a.part = static_cast<float*>(ws);
   a.out = out;
-  hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)(B * Hkv * a.S)), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)(B * Hkv * a.S));
+  if (a.G <= 1)
+    hipLaunchKernelGGL(attn_decode_kernel<1>, grid, dim3(256), 0, s, a);
+  else if (a.G <= 2)
+    hipLaunchKernelGGL(attn_decode_kernel<2>, grid, dim3(256), 0, s, a);
+  else if (a.G <= 4)
+    hipLaunchKernelGGL(attn_decode_kernel<4>, grid, dim3(256), 0, s, a);
+  else if (a.G <= 8)
+    hipLaunchKernelGGL(attn_decode_kernel<8>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_decode_kernel<16>, grid, dim3(256), 0, s, a);
   int rc = hip_status(hipGetLastError());
   if (rc) return rc;
   const long long waves = (long long)B * Hq;
