@@ -1075,24 +1075,13 @@ __device__ __forceinline__ void mirror_ready(const Guard& gd, Lds<MT, NS, NSLOT>
   const int l = lane_id();
   const int a0 = g0 & ~31;
   uint64_t t0 = 0;
-  constexpr int NIT = MAX_GROUPS / 64;
   for (;;) {
     bool all = true;
     const uint32_t err_ep = load_agent(gd.ctrl + C_ERR_EP);
-    // every flag's load issued before any is used: one round trip a pass
-    uint32_t f[NIT];
-#pragma unroll
-    for (int k = 0; k < NIT; ++k) {
-      const int i = a0 + 64 * k + l;
-      f[k] = i >= g0 && i < g1 ? load_agent(flags + i) : 0u;
-    }
-#pragma unroll
-    for (int k = 0; k < NIT; ++k) {
-      const int i0 = a0 + 64 * k;
-      if (i0 >= g1) break;
+    for (int i0 = a0; i0 < g1; i0 += 64) {
       const int i = i0 + l;
       const bool in = i >= g0 && i < g1;
-      const bool r = in && f[k] == gd.ep;
+      const bool r = in && load_agent(flags + i) == gd.ep;
       const uint64_t bal = __ballot(r);
       all = all && __all(r || !in);
       if (l == 0) {
@@ -1250,9 +1239,11 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
   const int l = lane_id();
   const Phase& ph = a.dn;
   // decode block: the residual stream's values of this band, loaded ahead of
-  // the split-K combine's round trips
-  float hv[2][MT][4];
-  if (a.h_out) {
+  // the split-K combine's round trips (up to 64 rows: at 128 the registers
+  // would spill, and they are loaded at the store instead)
+  constexpr bool PRE = MT <= 4;
+  float hv[2][PRE ? MT : 1][4];
+  if (PRE && a.h_out) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -1260,7 +1251,7 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int row = mt * 16 + 4 * (l >> 4) + rr;
-          hv[nb][mt][rr] = row < a.M ? a.h_in[(size_t)row * a.N + b * 32 + nb * 16 + (l & 15)] : 0.0f;
+          hv[nb][PRE ? mt : 0][rr] = row < a.M ? a.h_in[(size_t)row * a.N + b * 32 + nb * 16 + (l & 15)] : 0.0f;
         }
   }
   const int nsh = owner_wg(ph, b * ph.CPB + ph.CPB - 1) - owner_wg(ph, b * ph.CPB) + 1;
@@ -1278,7 +1269,7 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
         if (row < a.M) {
           const size_t o = (size_t)row * a.N + b * 32 + nb * 16 + (l & 15);
           if (a.h_out)  // residual epilogue: the bf16 output added to the fp32 stream
-            a.h_out[o] = hv[nb][mt][rr] + bf16_to_f32(f32_to_bf16(s[nb][mt][rr]));
+            a.h_out[o] = (PRE ? hv[nb][PRE ? mt : 0][rr] : a.h_in[o]) + bf16_to_f32(f32_to_bf16(s[nb][mt][rr]));
           else if (a.y32)
             a.y32[o] = s[nb][mt][rr];
           else
