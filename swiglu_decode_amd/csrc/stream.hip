@@ -1234,16 +1234,18 @@ __device__ void finish_gu_band(const Args& a, int b, v4f (&s)[2][MT], uint32_t e
   raise_flag(a.ctrl, PG_RDY, grp, ep);
 }
 
-template <int MT>
+// BLK: the decode block's residual epilogue (h_out = h_in + bf16(y)); a
+// separate instantiation, so that the plain MLP carries none of its code.
+template <int MT, bool BLK>
 __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2][MT]) {
   const int l = lane_id();
   const Phase& ph = a.dn;
   // decode block: the residual stream's values of this band, loaded ahead of
   // the split-K combine's round trips (up to 64 rows: at 128 the registers
   // would spill, and they are loaded at the store instead)
-  constexpr bool PRE = MT <= 4;
+  constexpr bool PRE = BLK && MT <= 4;
   float hv[2][PRE ? MT : 1][4];
-  if (PRE && a.h_out) {
+  if (PRE) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -1268,7 +1270,7 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
         const int row = mt * 16 + 4 * (l >> 4) + rr;
         if (row < a.M) {
           const size_t o = (size_t)row * a.N + b * 32 + nb * 16 + (l & 15);
-          if (a.h_out)  // residual epilogue: the bf16 output added to the fp32 stream
+          if (BLK)  // residual epilogue: the bf16 output added to the fp32 stream
             a.h_out[o] = (PRE ? hv[nb][PRE ? mt : 0][rr] : a.h_in[o]) + bf16_to_f32(f32_to_bf16(s[nb][mt][rr]));
           else if (a.y32)
             a.y32[o] = s[nb][mt][rr];
@@ -1348,7 +1350,7 @@ __device__ __forceinline__ void stage_activations(const Guard& gd, const Args& a
   }
 }
 
-template <int MT, int FMT, int XL, int NS, int NSLOT>
+template <int MT, int FMT, int XL, bool BLK, int NS, int NSLOT>
 __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, uint8_t* stages) {
   const int l = lane_id();
   const int W = blockIdx.x;
@@ -1359,7 +1361,7 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
   if (!XL) {
     // quantize this workgroup's share of x, then wait for everyone's
     // (the decode block's prologue has run already, flag included)
-    if (W < a.n_items && !a.h_in) {
+    if (W < a.n_items && !BLK) {
       xq_item<FMT>(a, W);
       drain_memory();
       raise_flag(a.ctrl, PG_XQ, W, ep);
@@ -1400,7 +1402,7 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
       for (int b = c0 / ph.CPB; b <= (c1 - 1) / ph.CPB; ++b) {
         v4f s[2][MT];
         take_event(gd, L, k++, s);
-        finish_dn_band<MT>(a, b, s);
+        finish_dn_band<MT, BLK>(a, b, s);
       }
     }
   }
@@ -1431,11 +1433,13 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
 // ---------------------------------------------------------------------------
 // XL: Q(x) is built in LDS by every workgroup (no cross-workgroup wait
 // before the first product); otherwise it is built once in the workspace.
-// MLP: the fused MLP (else the plain GEMM); separate kernels, so that each
-// gets its own register allocation.
+// MLP: 0 the plain GEMM, 1 the fused MLP, 2 the decode block (the fused MLP
+// with its RMSNorm prologue and residual epilogue); separate kernels, so that
+// each gets its own register allocation.
 template <int MT, int FMT, int XL, int MLP>
 __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) {
   using C = Cfg<MT>;
+  static_assert(MLP != 2 || !XL, "the decode block quantizes x into the workspace");
   __shared__ Lds<MT, C::NS, C::NSLOT> L;
   extern __shared__ __align__(16) uint8_t lds_x[];
   const int wv = uni((int)(threadIdx.x >> 6));
@@ -1450,7 +1454,7 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     L.abort = 0u;
   }
   __syncthreads();
-  if (MLP && !XL && a.h_in)
+  if (MLP == 2)
     block_prologue<FMT>(a, L.red, a.row_stash ? reinterpret_cast<float*>(lds_x) : nullptr, launch_epoch(a));
   if (wv == 0) {
     if (XL) {
@@ -1459,7 +1463,7 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
       xq.finish(a, lds_x, 16 * MT);
       __syncthreads();
     }
-    sync_wave<MT, FMT, XL>(a, L, lds_x);
+    sync_wave<MT, FMT, XL, MLP == 2>(a, L, lds_x);
   } else {
     const Guard gd{&L.abort, a.ctrl, a.budget, launch_epoch(a)};
     Streamer<MT, FMT, C::P, XL> st(a, wv - 1, lds_x, gd);
@@ -1643,27 +1647,40 @@ template <int MT, int FMT, int XL, int MLP>
 const void* kernel_ptr() { return reinterpret_cast<const void*>(&stream_kernel<MT, FMT, XL, MLP>); }
 
 // Kernel variants: (MT, XL) in (1,0) (1,1) (2,0) (2,1) (4,0) (8,0), each for
-// the MLP and for the plain GEMM.
-constexpr int NVAR = 12;
-int var_index(int MT, int XL, bool mlp) {
-  return (MT == 1 ? XL : MT == 2 ? 2 + XL : MT == 4 ? 4 : 5) + (mlp ? 6 : 0);
+// the plain GEMM (kind 0) and for the MLP (kind 1); the decode block (kind 2)
+// at MT 1, 2, 4, 8 with XL = 0.
+constexpr int NVAR = 16;
+int var_index(int MT, int XL, int kind) {
+  const int mi = MT == 1 ? 0 : MT == 2 ? 1 : MT == 4 ? 2 : 3;
+  if (kind == 2) return 12 + mi;
+  return (MT == 1 ? XL : MT == 2 ? 2 + XL : MT == 4 ? 4 : 5) + (kind ? 6 : 0);
 }
 
 template <int FMT, int MLP>
 const void* pick_fmt(int vi) {
-  switch (vi % 6) {
-    case 0: return kernel_ptr<1, FMT, 0, MLP>();
-    case 1: return kernel_ptr<1, FMT, 1, MLP>();
-    case 2: return kernel_ptr<2, FMT, 0, MLP>();
-    case 3: return kernel_ptr<2, FMT, 1, MLP>();
-    case 4: return kernel_ptr<4, FMT, 0, MLP>();
-    default: return kernel_ptr<8, FMT, 0, MLP>();
+  if constexpr (MLP == 2) {
+    switch (vi - 12) {
+      case 0: return kernel_ptr<1, FMT, 0, 2>();
+      case 1: return kernel_ptr<2, FMT, 0, 2>();
+      case 2: return kernel_ptr<4, FMT, 0, 2>();
+      default: return kernel_ptr<8, FMT, 0, 2>();
+    }
+  } else {
+    switch (vi % 6) {
+      case 0: return kernel_ptr<1, FMT, 0, MLP>();
+      case 1: return kernel_ptr<1, FMT, 1, MLP>();
+      case 2: return kernel_ptr<2, FMT, 0, MLP>();
+      case 3: return kernel_ptr<2, FMT, 1, MLP>();
+      case 4: return kernel_ptr<4, FMT, 0, MLP>();
+      default: return kernel_ptr<8, FMT, 0, MLP>();
+    }
   }
 }
-const void* pick_kernel(int MT, int fmt, int XL, bool mlp) {
-  const int vi = var_index(MT, XL, mlp);
-  if (fmt == FMT_BLOCK) return mlp ? pick_fmt<FMT_BLOCK, 1>(vi) : pick_fmt<FMT_BLOCK, 0>(vi);
-  return mlp ? pick_fmt<FMT_MX, 1>(vi) : pick_fmt<FMT_MX, 0>(vi);
+const void* pick_kernel(int MT, int fmt, int XL, int kind) {
+  const int vi = var_index(MT, XL, kind);
+  if (fmt == FMT_BLOCK)
+    return kind == 2 ? pick_fmt<FMT_BLOCK, 2>(vi) : kind ? pick_fmt<FMT_BLOCK, 1>(vi) : pick_fmt<FMT_BLOCK, 0>(vi);
+  return kind == 2 ? pick_fmt<FMT_MX, 2>(vi) : kind ? pick_fmt<FMT_MX, 1>(vi) : pick_fmt<FMT_MX, 0>(vi);
 }
 
 constexpr int LDS_PER_WG = 163840;  // gfx950: 160 KB of LDS per workgroup
@@ -1698,11 +1715,11 @@ Occupancy g_occ;
 
 // The XL variants may use up to all LDS the static part leaves; the
 // occupancy is taken at that maximum, so it holds for any smaller use.
-int grid_size(int MT, int fmt, int XL, bool mlp, int* out) {
+int grid_size(int MT, int fmt, int XL, int kind, int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SGD_EHIP;
   const int fi = fmt == FMT_BLOCK ? 0 : 1;
-  const int vi = var_index(MT, XL, mlp);
+  const int vi = var_index(MT, XL, kind);
   std::lock_guard<std::mutex> lock(g_occ.mu);
   if (g_occ.cus[dev] == 0) {
     int cus = 0;
@@ -1711,8 +1728,8 @@ int grid_size(int MT, int fmt, int XL, bool mlp, int* out) {
     g_occ.cus[dev] = cus;
   }
   if (g_occ.per_cu[dev][fi][vi] == 0) {
-    const void* kern = pick_kernel(MT, fmt, XL, mlp);
-    const int dyn = XL ? LDS_PER_WG - (int)static_lds(MT) : ks_dyn(MT, mlp);
+    const void* kern = pick_kernel(MT, fmt, XL, kind);
+    const int dyn = XL ? LDS_PER_WG - (int)static_lds(MT) : ks_dyn(MT, kind != 0);
     // (any variant may be launched with up to all the LDS its static part
     // leaves: the decode block's row stash)
     if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WG - (int)static_lds(MT)) !=
@@ -1783,8 +1800,14 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   // (the decode block runs on the grid of the plain MLP's kernel: the same
   // split of the work, so the same sums, bit for bit)
   int G = 0;
-  int rc = grid_size(MT, pr.fmt, plain_xl, mlp, &G);
+  int rc = grid_size(MT, pr.fmt, plain_xl, mlp ? 1 : 0, &G);
   if (rc != SGD_OK) return rc;
+  if (pr.h_in) {
+    // the block's own kernel must fit one workgroup per compute unit
+    int Gb = 0;
+    rc = grid_size(MT, pr.fmt, 0, 2, &Gb);
+    if (rc != SGD_OK) return rc;
+  }
   if (pr.h_in && !plain_xl) {
     // one workgroup per compute unit, which the row stash always leaves room for
     int dev = 0;
@@ -1864,7 +1887,8 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.gu = p.gu;
   a.dn = p.dn;
   void* args[] = {&a};
-  return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt, XL, mlp), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, dyn, s));
+  const int kind = pr.h_in ? 2 : mlp ? 1 : 0;
+  return hip_status(hipLaunchKernel(pick_kernel(p.MT, pr.fmt, XL, kind), dim3(G), dim3(64 * cfg_nwave(p.MT)), args, dyn, s));
 }
 
 }  // namespace sgd
