@@ -16,10 +16,12 @@
 // reads its operands with two 16-byte LDS reads per tile.
 //
 // Kernel.  A workgroup computes a BM x BN block of C = Q(x) W^T over all of
-// K, k-tile by k-tile through two LDS stages: while the matrix cores work on
-// stage kt, k-tile kt+1 is copied into the other stage by direct
-// memory-to-LDS loads (no registers; waited for before the one barrier per
-// k-tile).  Wavefront
+// K, k-tile by k-tile through NSTG LDS stages: while the matrix cores work on
+// stage kt, k-tiles kt+1 .. kt+NSTG-1 are on their way into the other stages
+// by direct memory-to-LDS loads (no registers), the operand tiles and their
+// scales alike, and one barrier per k-tile hands a stage over.  With two
+// stages the copies' latency, not the matrix cores, set the pace (measured:
+// 1.1 PFLOP/s at 8192^3; three stages of 256 x 128 give 1.7).  Wavefront
 // (wm, wn) owns TM m-tiles x TN n-blocks.  MX: the E8M0 scales go into the
 // instruction; block format: the unscaled product of each k-tile is added
 // with the row's activation scale times the weight block's scale, as in the
@@ -53,22 +55,50 @@ __device__ __forceinline__ int uni_t(int v) { return __builtin_amdgcn_readfirstl
 // 1 KB from memory straight into LDS: lane l's 16 bytes at buffer offset
 // voff land at LDS byte m0 + 16*l.  Written as the instruction itself so that
 // the compiler does not wait for it before unrelated LDS reads; the kernel
-// waits for these copies itself (lds_copies_done) before its barrier.  No
+// waits for these copies itself (lds_copies_left) before its barrier.  No
 // register receives data.
 __device__ __forceinline__ void lds_copy1k(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_copies_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int FMT, int WGM, int WGN, int TM, int TN, int KS, int OUT>
+// 256 bytes from memory straight into LDS: lane l's dword at buffer offset
+// voff lands at LDS byte m0 + 4*l (the scales of a stage).
+__device__ __forceinline__ void lds_copy256(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+// Wait until at most N of this wavefront's memory loads are in flight (loads
+// complete in issue order, so every copy issued before the last N is done).
+template <int N>
+__device__ __forceinline__ void lds_copies_left() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS stage of the tiled GEMM: the k-tile's AT activation tiles and BT weight
+// tiles (2 KB each, A first), then the scales: 64 bytes per m-tile (mx: the
+// rows' E8M0 bytes of the k-tile's four 32-column blocks, row-major; block:
+// the 16 rows' fp32 scales), then 256 bytes per n-tile (mx: the dword of 4
+// k-tiles of each lane's row, as packed; block: one fp32 per 128-row weight
+// block of the workgroup).
+template <int AT, int BT>
+__host__ __device__ constexpr int tile_stage_bytes() { return (AT + BT) * 2048 + AT * 64 + BT * 256; }
+constexpr int TRASH_BYTES = 256;  // where the copies that only pad the per-wavefront count land
+
+template <int FMT, int WGM, int WGN, int TM, int TN, int NSTG, int OUT>
 __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
   constexpr int AT = WGM * TM, BT = WGN * TN;  // A and B tiles of one k-tile
-  constexpr int ST = KS * (AT + BT);           // tiles of a stage (KS k-tiles)
   constexpr int NW = WGM * WGN;
-  constexpr int CH = 2 * ST / NW;         // 1 KB halves of tiles each wavefront copies per stage
-  static_assert(2 * ST % NW == 0, "stage halves");
+  constexpr int CH = 2 * (AT + BT) / NW;       // 1 KB tile halves each wavefront copies per stage
+  static_assert(2 * (AT + BT) % NW == 0, "stage halves");
+  static_assert(AT % 4 == 0 && BT % 8 == 0, "scale copies");
+  constexpr int SC = AT / 4 + (FMT == FMT_MX ? BT : 1);  // 256-byte scale copies per stage
+  constexpr int SCH = (SC + NW - 1) / NW;                 // per wavefront (padded)
+  constexpr int OPS = CH + SCH;                           // copies per wavefront per stage
+  constexpr int SB = tile_stage_bytes<AT, BT>();
+  static_assert(NSTG >= 2, "stages");
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds;
+  const uint32_t trash = lds0 + (uint32_t)(NSTG * SB);
   const int l = lane_id(), wv = uni_t((int)(threadIdx.x >> 6));
   const int wm = wv % WGM, wn = wv / WGM;
   const int bm = blockIdx.x % p.tiles_m, bn = blockIdx.x / p.tiles_m;
@@ -78,67 +108,56 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(p.as, p.as_bytes), rws = make_rsrc(p.ws, p.ws_bytes);
   const int MTA = p.Mpad >> 4, NBW = p.N >> 4;
 
-  // ---- stage copy: wavefront wv copies halves wv, wv + NW, ... of the
-  // stage's ST tiles: k-tile kt0 + u of the stage holds tiles
-  // u*(AT+BT) .. (u+1)*(AT+BT)-1, A first (tiles past the matrices, or k-tiles
-  // past K, read zeros) ----
-  auto copy_stage = [&](int kt0, int s) {
+  // ---- stage copy: k-tile kt into stage buffer b.  Wavefront wv copies tile
+  // halves wv, wv + NW, ... and scale blocks wv, wv + NW, ...; every
+  // wavefront issues exactly OPS copies (k-tiles past K, tiles past the
+  // matrices and the padding read zeros), so that the number of copies in
+  // flight behind a stage is the same for all ----
+  auto copy_stage = [&](int kt, int b) {
+    const uint32_t base = lds0 + (uint32_t)(b * SB);
+    const bool in = kt < KT;
+    const uint32_t ukt = in ? (uint32_t)kt : 0u;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int h = wv + NW * i, tt = h >> 1, half = h & 1;
-      const int u = tt / (AT + BT), t = tt - u * (AT + BT), kt = kt0 + u;
-      const uint32_t m0 = lds0 + (uint32_t)((s * ST + tt) * 2048 + half * 1024);
+      const int h = wv + NW * i, t = h >> 1, half = h & 1;
+      const uint32_t m0 = base + (uint32_t)(t * 2048 + half * 1024);
       const uint32_t lo = (uint32_t)half * 1024u + (uint32_t)l * 16u;
-      if (kt >= KT) {
-        lds_copy1k(ra, m0, OOB_T);
-      } else if (t < AT) {
+      if (t < AT) {
         const int mt = mt0 + t;
-        lds_copy1k(ra, m0, mt < MTA ? (uint32_t)mt * 16u * (uint32_t)p.K + (uint32_t)kt * 2048u + lo : OOB_T);
+        lds_copy1k(ra, m0, in && mt < MTA ? (uint32_t)mt * 16u * (uint32_t)p.K + ukt * 2048u + lo : OOB_T);
       } else {
         const int nb = nb0 + t - AT;
-        lds_copy1k(rw, m0, nb < NBW ? ((uint32_t)nb * (uint32_t)KT + (uint32_t)kt) * 2048u + lo : OOB_T);
+        lds_copy1k(rw, m0, in && nb < NBW ? ((uint32_t)nb * (uint32_t)KT + ukt) * 2048u + lo : OOB_T);
       }
     }
-  };
-
-  // ---- this wavefront's scales for one k-tile ----
-  // mx: the activation scale byte of (row l%16, block l/16) per m-tile, and
-  // the weight's dword of 4 k-tiles per n-block (the k-tile's byte selected
-  // at use); block: the activation scales of rows 4(l/16)..+3 per m-tile and
-  // the 128x128 weight block's scale (one per wavefront: TN*16 <= 128 rows
-  // aligned to 128).
-  struct Scales {
-    uint32_t xa[TM];
-    v4f xb[TM];
-    uint32_t wsd[TN];
-    float wbs;
-  };
-  auto load_scales = [&](int kt, Scales& sc) {
+    const uint32_t sbase = base + (uint32_t)((AT + BT) * 2048);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int mt = mt0 + wm * TM + i;
-      const bool ok = mt < MTA;
-      if (FMT == FMT_MX) {
-        const uint32_t o = (uint32_t)mt * 16u * (uint32_t)(p.K >> 5) + (uint32_t)kt * 64u + (uint32_t)(l & 15) * 4u +
-                           (uint32_t)(l >> 4);
-        sc.xa[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ras, ok ? o : OOB_T, 0, 0);
+    for (int i = 0; i < SCH; ++i) {
+      const int c = wv + NW * i;
+      if (c < AT / 4) {
+        // m-tiles mt0 + 4c .. +3: lane l carries (m-tile 4c + l/16, dword l%16)
+        const int mt = mt0 + 4 * c + (l >> 4);
+        const bool ok = in && mt < MTA;
+        const uint32_t o = FMT == FMT_MX
+                               ? (uint32_t)mt * 16u * (uint32_t)(p.K >> 5) + ukt * 64u + (uint32_t)(l & 15) * 4u
+                               : (ukt * (uint32_t)p.Mpad + (uint32_t)mt * 16u + (uint32_t)(l & 15)) * 4u;
+        lds_copy256(ras, sbase + (uint32_t)(c * 256), ok ? o : OOB_T);
+      } else if (c < SC) {
+        const uint32_t dst = sbase + (uint32_t)(AT * 64 + (c - AT / 4) * 256);
+        if (FMT == FMT_MX) {
+          const int nb = nb0 + c - AT / 4;
+          const uint32_t KG = (uint32_t)(KT + 3) >> 2;
+          const uint32_t o = ((uint32_t)nb * KG + (ukt >> 2)) * 256u + (uint32_t)l * 4u;
+          lds_copy256(rws, dst, in && nb < NBW ? o : OOB_T);
+        } else {
+          // lane j: the scale of the workgroup's j-th 128-row weight block
+          const int blk = (nb0 >> 3) + l;
+          const bool ok = in && l < BT / 8 && blk * 8 < NBW;
+          lds_copy256(rws, dst, ok ? ((uint32_t)blk * (uint32_t)KT + ukt) * 4u : OOB_T);
+        }
       } else {
-        const uint32_t o = ((uint32_t)kt * (uint32_t)p.Mpad + (uint32_t)mt * 16u + 4u * (uint32_t)(l >> 4)) * 4u;
-        sc.xb[i] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(ras, ok ? o : OOB_T, 0, 0));
+        lds_copy256(ras, trash, OOB_T);
       }
-    }
-    if (FMT == FMT_MX) {
-      const uint32_t KG = (uint32_t)(KT + 3) >> 2;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int nb = nb0 + wn * TN + j;
-        const uint32_t o = ((uint32_t)nb * KG + (uint32_t)(kt >> 2)) * 256u + (uint32_t)l * 4u;
-        sc.wsd[j] = __builtin_amdgcn_raw_buffer_load_b32(rws, nb < NBW ? o : OOB_T, 0, 0);
-      }
-    } else {
-      const int nb = nb0 + wn * TN;
-      const uint32_t o = ((uint32_t)(nb >> 3) * (uint32_t)KT + (uint32_t)kt) * 4u;
-      sc.wbs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rws, nb < NBW ? o : OOB_T, 0, 0));
     }
   };
 
@@ -148,57 +167,51 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  Scales sc_cur[KS], sc_next[KS];
-  copy_stage(0, 0);
+  // NSTG - 1 stages in flight ahead of the one being multiplied; one barrier
+  // per k-tile both publishes stage kt (every wavefront has waited for its
+  // own copies of it) and frees stage kt - 1 for the copy of kt + NSTG - 1
 #pragma unroll
-  for (int u = 0; u < KS; ++u) load_scales(u, sc_cur[u]);
-  lds_copies_done();
-  __syncthreads();
-  for (int kt0 = 0; kt0 < KT; kt0 += KS) {
-    const bool more = kt0 + KS < KT;
-    if (more) {
-      // (the other stage was last read in the previous stage's k-tiles, before its barrier)
-      copy_stage(kt0 + KS, (kt0 / KS + 1) & 1);
+  for (int b = 0; b < NSTG - 1; ++b) copy_stage(b, b);
+  for (int kt = 0; kt < KT; ++kt) {
+    lds_copies_left<(NSTG - 2) * OPS>();
+    __syncthreads();
+    copy_stage(kt + NSTG - 1, (kt + NSTG - 1) % NSTG);
+    const uint8_t* st = lds + (kt % NSTG) * SB;
+    const uint8_t* ssa = st + (AT + BT) * 2048;
+    const uint8_t* ssb = ssa + AT * 64;
+    v8i av[TM];
+    uint32_t xa[TM];
+    v4f xb[TM];
 #pragma unroll
-      for (int u = 0; u < KS; ++u) load_scales(kt0 + KS + u, sc_next[u]);
+    for (int i = 0; i < TM; ++i) {
+      const int ti = wm * TM + i;
+      const uint8_t* t = st + ti * 2048 + l * 16;
+      av[i] = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
+      if (FMT == FMT_MX)
+        xa[i] = (uint32_t)ssa[ti * 64 + (l & 15) * 4 + (l >> 4)];
+      else
+        xb[i] = *reinterpret_cast<const v4f*>(ssa + ti * 64 + 16 * (l >> 4));
     }
-    const uint8_t* st0 = lds + ((kt0 / KS) & 1) * ST * 2048;
+    const int sh = 8 * (kt & 3);
+    const float wbs = FMT == FMT_MX ? 1.0f : reinterpret_cast<const float*>(ssb)[(wn * TN) >> 3];
 #pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      const int kt = kt0 + u;
-      if (kt >= KT) break;
-      const uint8_t* st = st0 + u * (AT + BT) * 2048;
-      const Scales& sc = sc_cur[u];
-      v8i av[TM];
+    for (int j = 0; j < TN; ++j) {
+      const uint8_t* t = st + (AT + wn * TN + j) * 2048 + l * 16;
+      const v8i bv = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
+      const uint32_t wsd = FMT == FMT_MX ? reinterpret_cast<const uint32_t*>(ssb)[(wn * TN + j) * 64 + l] : 0u;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const uint8_t* t = st + (wm * TM + i) * 2048 + l * 16;
-        av[i] = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
-      }
-      const int sh = 8 * (kt & 3);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint8_t* t = st + (AT + wn * TN + j) * 2048 + l * 16;
-        const v8i bv = make_v8i(*reinterpret_cast<const uint4*>(t), *reinterpret_cast<const uint4*>(t + 1024));
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          if (FMT == FMT_MX) {
-            acc[i][j] = mfma_f8(av[i], bv, acc[i][j], (int)sc.xa[i], (int)(sc.wsd[j] >> sh));
-          } else {
-            const v4f z = {0.f, 0.f, 0.f, 0.f};
-            const v4f t4 = mfma_f8(av[i], bv, z, 127, 127);
-            acc[i][j] += t4 * (sc.xb[i] * sc.wbs);
-          }
+        if (FMT == FMT_MX) {
+          acc[i][j] = mfma_f8(av[i], bv, acc[i][j], (int)xa[i], (int)(wsd >> sh));
+        } else {
+          const v4f z = {0.f, 0.f, 0.f, 0.f};
+          const v4f t4 = mfma_f8(av[i], bv, z, 127, 127);
+          acc[i][j] += t4 * (xb[i] * wbs);
         }
       }
     }
-    lds_copies_done();
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < KS; ++u) sc_cur[u] = sc_next[u];
-    }
   }
+  lds_copies_left<0>();  // (the fillers' copies: nothing may be in flight at exit)
 
   // ---- epilogue: rows < M, columns < N ----
 #pragma unroll
@@ -267,13 +280,14 @@ __global__ __launch_bounds__(256) void act_tiles_kernel(const uint16_t* __restri
   }
 }
 
-template <int FMT, int WGM, int WGN, int TM, int TN, int KS, int OUT>
+template <int FMT, int WGM, int WGN, int TM, int TN, int NSTG, int OUT>
 int launch_tile_cfg(TileArgs p, hipStream_t s) {
   constexpr int BM = WGM * TM * 16, BN = WGN * TN * 16;
-  constexpr size_t lds = 2 * (size_t)KS * (WGM * TM + WGN * TN) * 2048;
+  constexpr size_t lds = (size_t)NSTG * tile_stage_bytes<WGM * TM, WGN * TN>() + TRASH_BYTES;
+  static_assert(lds <= 163840, "LDS of one workgroup");
   p.tiles_m = (p.Mpad + BM - 1) / BM;
   const long long grid = (long long)p.tiles_m * ((p.N + BN - 1) / BN);
-  auto k = tile_gemm_kernel<FMT, WGM, WGN, TM, TN, KS, OUT>;
+  auto k = tile_gemm_kernel<FMT, WGM, WGN, TM, TN, NSTG, OUT>;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
       hipSuccess)
     return SGD_EHIP;
@@ -283,8 +297,8 @@ int launch_tile_cfg(TileArgs p, hipStream_t s) {
 
 template <int FMT, int OUT>
 int launch_tile_gemm_fmt(const TileArgs& a, bool big, hipStream_t s) {
-  if (big) return launch_tile_cfg<FMT, 4, 2, 4, 4, 1, OUT>(a, s);  // 256 x 128 blocks, 8 wavefronts of 64 x 64
-  return launch_tile_cfg<FMT, 2, 2, 4, 4, 1, OUT>(a, s);           // 128 x 128 blocks, 4 wavefronts of 64 x 64
+  if (big) return launch_tile_cfg<FMT, 4, 2, 4, 4, 3, OUT>(a, s);  // 256 x 128 blocks, 8 wavefronts of 64 x 64, 3 stages
+  return launch_tile_cfg<FMT, 2, 2, 4, 4, 4, OUT>(a, s);           // 128 x 128 blocks, 4 wavefronts of 64 x 64, 4 stages
 }
 
 }  // namespace

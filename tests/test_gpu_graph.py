@@ -1,4 +1,4 @@
-"""The fused MLP and the scaled GEMM captured in a HIP graph: several replays,
+"""The fused MLP and the scaled GEMM captured in a HIP graph: 100 replays,
 with eager work and synchronisations between them, each equal to the eager
 result bit for bit (the kernels leave the workspace's control block ready
 for the next launch, with counters zero and flags holding the launch number,
@@ -14,7 +14,7 @@ from tests.gpu_util import dev, note
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fmt,M", [("block", 4), ("mx", 16), ("mx", 64)])
+@pytest.mark.parametrize("fmt,M", [("block", 4), ("mx", 16), ("mx", 64), ("block", 128)])
 def test_graph_replay_matches_eager(fmt, M):
     d = dev()
     note(f"graph replay {fmt} M={M}")
@@ -36,7 +36,7 @@ def test_graph_replay_matches_eager(fmt, M):
         with torch.cuda.graph(graph, stream=st):
             sgd.fused_swiglu_mlp(x, *pws, out=y, workspace=ws)
             sgd.scaled_gemm(x, pws[0], out=g, workspace=ws)
-        for r in range(4):
+        for r in range(100):
             y.zero_()
             g.zero_()
             st.synchronize()
