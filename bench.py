@@ -520,7 +520,7 @@ def regression(per_m, d2048):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=25)  # 25 graph replays of 8 launches: 200 timed calls at d=4096
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--ms", default="1,16,64,128")
     ap.add_argument("--fmt", default="mx")

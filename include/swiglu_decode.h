@@ -430,6 +430,12 @@ int sgd_scaled_gemm_q(const uint8_t* xq, const void* xs, int M,
                       size_t ws_bytes, void* stream);
 
 /* ---- decode-stack glue (pre-RMSNorm residual blocks + output head) ----- */
+/* These calls serve the 24-block decode-stack workload only (24 pre-RMSNorm
+ * residual SwiGLU blocks at d=2560, ffn=9728, then a bf16 output head and a
+ * per-row argmax).  The pages describe the MLP, not the layers around it:
+ * no passage defines these operations; each comment states the definition
+ * used.  Errors: SGD_EINVAL (null pointer, M or shape out of range),
+ * SGD_EALIGN, SGD_EDIM. */
 /* h [M, d] fp32 <- x [M, d] bf16 (exact widening).  d multiple of 128. */
 int sgd_bf16_to_f32(const uint16_t* x_bf16, int M, int d, float* h, void* stream);
 
