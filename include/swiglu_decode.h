@@ -343,8 +343,10 @@ int sgd_swiglu_mlp_prefill(const uint16_t* x_bf16, int M, const sgd_weight* gate
  *   K: bytes 0..2047: the 16 x 128 operand tile of the slots (lane l = r + 16q
  *      holds slot r, dims 16q..16q+15 at bytes 16l.. and dims 64+16q..
  *      at 1024 + 16l..); bytes 2048 + l: scale of (slot l % 16, block l / 16).
- *   V: byte 32i + 2r + e: code of (slot r, dim 2i + e), i < 64; bytes
- *      2048 + 16b + r: scale of (slot r, block b).
+ *   V: byte 32l + 4n + (r % 4), l = (d % 16) + 16 (r / 4): code of
+ *      (slot r, dim d = 16n + d % 16), n < 8 (each lane's 32 bytes hold four
+ *      consecutive slots of its dims); byte 2048 + 16 (r / 4) + 4b + r % 4:
+ *      scale of (slot r, block b).
  * Slot s of a sequence's token t is page block_table[b][t / 16], slot t % 16.
  */
 

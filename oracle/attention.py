@@ -80,9 +80,11 @@ def decode_attention(q, k, v, seq_lens, sm_scale=None):
 #    lane l = r + 16 q (slot r, q = 0..3) has dims 16q..16q+15 at bytes
 #    16l..16l+15 and dims 64+16q..64+16q+15 at bytes 1024+16l..1024+16l+15;
 #    bytes 2048 + l: the E8M0 scale of slot l % 16, 32-dim block l // 16.
-# V: bytes 0..2047: byte 32 i + 2 r + e is the code of slot r, dim 2i + e
-#    (i = 0..63, e = 0, 1); bytes 2048 + 16 b + r: the scale of slot r,
-#    block b.
+# V: bytes 0..2047: lane l = (d % 16) + 16 (r // 4) holds bytes 32 l..32 l+31:
+#    byte 32 l + 4 n + (r % 4) is the code of slot r, dim d = 16 n + d % 16
+#    (n = 0..7), i.e. per lane and 16-dim block n one dword of four
+#    consecutive slots; byte 2048 + 16 (r // 4) + 4 b + r % 4: the scale of
+#    slot r, block b (lane group r // 4 reads its 16 scale bytes at once).
 def page_bytes(D=HEAD_DIM):
     return D * PAGE + PAGE * (D // 32)
 
@@ -101,12 +103,12 @@ def _k_tile(codes, scales):
 def _v_tile(codes, scales):
     """codes [16, 128], scales [16, 4] -> 2112 bytes (V layout)."""
     out = np.zeros(page_bytes(), dtype=np.uint8)
-    for i in range(64):
-        for r in range(16):
-            out[32 * i + 2 * r] = codes[r, 2 * i]
-            out[32 * i + 2 * r + 1] = codes[r, 2 * i + 1]
-    for b in range(4):
-        out[2048 + 16 * b:2048 + 16 * b + 16] = scales[:, b]
+    for r in range(16):
+        for d in range(HEAD_DIM):
+            lane = d % 16 + 16 * (r // 4)
+            out[32 * lane + 4 * (d // 16) + r % 4] = codes[r, d]
+        for b in range(4):
+            out[2048 + 16 * (r // 4) + 4 * b + r % 4] = scales[r, b]
     return out
 
 

@@ -12,9 +12,12 @@
 //      instruction (lane l = r + 16q: slot r, dims 16q.. and 64+16q..), then
 //      64 scale bytes, byte l = (slot l % 16, block l / 16): the instruction's
 //      scale operand, one byte per lane;
-//   V: byte 32i + 2r + e = (slot r, dim 2i + e), so lane i reads its two dims
-//      of all 16 slots as 32 contiguous bytes; then byte 16b + r = the scale
-//      of (slot r, block b).
+//   V: lane l = (d % 16) + 16 (r / 4) holds 32 bytes, byte 4n + r % 4 the code
+//      of (slot r, dim 16n + d % 16): per 16-dim block n one dword of four
+//      consecutive slots, the operand order of a 16x16x16 bf16 matrix
+//      instruction's B operand (V as slots x dims); then byte
+//      16 (r / 4) + 4b + r % 4 = the scale of (slot r, block b), the 16 bytes
+//      of one lane group together.
 //
 // Decode.  A workgroup takes one (sequence, KV head) and one of S splits of
 // the sequence's pages; its four wavefronts take every fourth page of the
@@ -23,7 +26,8 @@
 // against the page's 16 slots, the K tile being the shared operand (the
 // stride-0 broadcast); the online softmax (fp32, exp2, scores pre-multiplied
 // by sm_scale * log2 e) is updated once per RING pages; then o += p V on the
-// vector units, V widened exactly from E4M3 with its scale.
+// bf16 matrix instruction: V's E4M3 codes widened exactly to bf16, its
+// per-(slot, block) scale folded into p (rounded to bf16) by ldexp.
 // The four wavefronts' states are merged in LDS into the split's partial
 // (row max, row sum, unnormalized o); a second kernel merges the splits and
 // writes bf16.  The work is HBM-bound: one pass over the sequence's K and V.
@@ -43,6 +47,10 @@ constexpr int RING = 2;               // pages in flight per wavefront (4 and 8 
 constexpr int MAXCHUNK = 1024;        // pages of one split (their ids are staged in LDS)
 constexpr float LOG2E = 1.4426950408889634f;
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
 struct AttnArgs {
   const uint16_t* q;   // [B, Hq, 128] bf16
   const uint8_t* kc;   // [n_pages, Hkv, 2112]
@@ -55,7 +63,6 @@ struct AttnArgs {
   uint16_t* out;       // [B, Hq, 128] bf16
 };
 
-__device__ __forceinline__ float e8m0_value(uint32_t b) { return pow2_pos((int)(b & 0xFFu) - 127); }
 
 // Max / sum over each row of 16 lanes, every lane of the row receiving the
 // result: lane exchanges within quads (swap neighbours, then pairs), then
@@ -121,13 +128,16 @@ __global__ __launch_bounds__(256) void kv_write_kernel(int kind, const uint16_t*
     }
     base[2048 + r + 16 * j] = (uint8_t)se;
   } else {
-    // dim pair i = 16j + k: bytes 32i + 2r, 32i + 2r + 1
+    // dim d = 32j + 4k + e (byte e of cw[k]): lane (d % 16) + 16 (r / 4),
+    // byte 4 (d / 16) + r % 4
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t pair = (cw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-      *reinterpret_cast<uint16_t*>(base + 32 * (16 * j + k) + 2 * r) = (uint16_t)pair;
-    }
-    base[2048 + 16 * j + r] = (uint8_t)se;
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 32 * j + 4 * k + e;
+        base[32 * ((d & 15) + 16 * (r >> 2)) + 4 * (d >> 4) + (r & 3)] = (uint8_t)(cw[k] >> (8 * e));
+      }
+    base[2048 + 16 * (r >> 2) + 4 * j + (r & 3)] = (uint8_t)se;
   }
 }
 
@@ -144,7 +154,6 @@ struct AttnLds {
   int ids[MAXCHUNK];          // physical pages of this split
 };
 
-template <int NG>  // query heads per KV head, rounded up to a power of two (<= 16)
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   __shared__ AttnLds L;
   const int l = lane_id(), wv = (int)(threadIdx.x >> 6);
@@ -195,17 +204,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   const int qsc = L.qs[l];
 
   // this wavefront's state: per head (row 4(l/16) + rr of the scores, held
-  // alike by the 16 lanes of a row group) the running max and sum; per lane
-  // o of dims 2l, 2l+1 for every head
+  // alike by the 16 lanes of a row group) the running max and sum; o as the
+  // matrix instruction's accumulators, 16-dim block n: heads 4(l/16) + rr,
+  // dim 16n + l % 16
   float mrow[4], lrow[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     mrow[rr] = -INFINITY;
     lrow[rr] = 0.0f;
   }
-  float o[NG][2];
+  v4f o[8];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) o[g][0] = o[g][1] = 0.0f;
+  for (int n = 0; n < 8; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t cache_bytes = (uint32_t)a.n_pages * (uint32_t)a.Hkv * (uint32_t)PAGE_BYTES;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc, cache_bytes), rv = make_rsrc(a.vc, cache_bytes);
@@ -227,7 +237,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     R[u].ks = __builtin_amdgcn_raw_buffer_load_b8(rk, in ? base + 2048 + l : base, 0, 0);
     R[u].v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + l * 32 : base, 0, AUX_NT));
     R[u].v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + l * 32 + 16 : base, 0, AUX_NT));
-    R[u].vs = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + 2048 + 16 * (l >> 4) : base, 0, 0));
+    R[u].vs = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + 2048 + 16 * (l >> 4) : base, 0, 0));  // (this lane group's slots)
   };
   int p = p0 + wv;
 #pragma unroll
@@ -268,48 +278,41 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     }
     // (LDS writes and reads of one wavefront complete in program order)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    {
+      const v4f al = *reinterpret_cast<const v4f*>(&L.alpha[wv][4 * (l >> 4)]);
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-      if (g < G) {
-        const float al = L.alpha[wv][g];
-        o[g][0] *= al;
-        o[g][1] *= al;
-      }
-    // o += p V page by page (dims 2l, 2l+1; V of slots past the length is
-    // zero), each page's loads reissued for the next step once used
+      for (int n = 0; n < 8; ++n) o[n] *= al;
+    }
+    // o += p V page by page on the matrix unit: A = p (head l % 16, slots
+    // 4(l/16)..+3) times V's scale of (slot, 32-dim block), one operand per
+    // block; B = V's codes (slots 4(l/16)..+3, dim 16n + l % 16).  Slots past
+    // the length have p = 0 and zeroed codes (a stale slot may hold NaN
+    // codes).  Each page's loads are reissued for the next step once used.
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
       const int pg = p + 4 * u;
       if (pg < p1) {
-        float v[PSLOTS][2];
-        const uint32_t vw[8] = {R[u].v0.x, R[u].v0.y, R[u].v0.z, R[u].v0.w, R[u].v1.x, R[u].v1.y, R[u].v1.z, R[u].v1.w};
+        const v4f pp = *reinterpret_cast<const v4f*>(&L.p[wv][l & 15][u * PSLOTS + 4 * (l >> 4)]);
         const uint32_t vsw[4] = {R[u].vs.x, R[u].vs.y, R[u].vs.z, R[u].vs.w};
-        const bool full = (pg + 1) * PSLOTS <= T;
+        v4s pa[4];
 #pragma unroll
-        for (int r = 0; r < PSLOTS; ++r) {
-          const float scl = e8m0_value(vsw[r >> 2] >> (8 * (r & 3)));
-          const auto f = (r & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vw[r >> 1], scl, true)
-                                 : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)vw[r >> 1], scl, false);
-          const bool lv = full || pg * PSLOTS + r < T;
-          v[r][0] = lv ? f[0] : 0.0f;
-          v[r][1] = lv ? f[1] : 0.0f;
+        for (int bk = 0; bk < 4; ++bk) {
+          v4bf t;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            t[j] = (__bf16)__builtin_amdgcn_ldexpf(pp[j], (int)((vsw[bk] >> (8 * j)) & 0xFFu) - 127);
+          pa[bk] = __builtin_bit_cast(v4s, t);
         }
+        const int live = T - (pg * PSLOTS + 4 * (l >> 4));  // slots of this lane group within the length
+        const uint32_t keep = live >= 4 ? 0xFFFFFFFFu : live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - live)));
+        const uint32_t vw[8] = {R[u].v0.x, R[u].v0.y, R[u].v0.z, R[u].v0.w, R[u].v1.x, R[u].v1.y, R[u].v1.z, R[u].v1.w};
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          if (g < G) {
-            float a0 = o[g][0], a1 = o[g][1];
-#pragma unroll
-            for (int r4 = 0; r4 < PSLOTS; r4 += 4) {
-              const v4f pp = *reinterpret_cast<const v4f*>(&L.p[wv][g][u * PSLOTS + r4]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                a0 = fmaf(pp[e], v[r4 + e][0], a0);
-                a1 = fmaf(pp[e], v[r4 + e][1], a1);
-              }
-            }
-            o[g][0] = a0;
-            o[g][1] = a1;
-          }
+        for (int n = 0; n < 8; ++n) {
+          const uint32_t w = vw[n] & keep;
+          const v2bf b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+          const v2bf b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+          const v4bf bv = {b0[0], b0[1], b1[0], b1[1]};
+          o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[n >> 1], __builtin_bit_cast(v4s, bv), o[n], 0, 0, 0);
         }
       }
       issue(u, pg + 4 * RING);
@@ -327,8 +330,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     }
   }
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
-    if (g < G) *reinterpret_cast<float2*>(&L.o[wv][g][2 * l]) = make_float2(o[g][0], o[g][1]);
+  for (int n = 0; n < 8; ++n)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int g = 4 * (l >> 4) + rr;
+      if (g < G) L.o[wv][g][16 * n + (l & 15)] = o[n][rr];
+    }
   __syncthreads();
   float* part = a.part + (size_t)blockIdx.x * G * (2 + HD);
   for (int i = threadIdx.x; i < G * HD; i += 256) {
@@ -427,16 +434,7 @@ int launch_paged_decode(const uint16_t* q, const uint8_t* kc, const uint8_t* vc,
   a.part = static_cast<float*>(ws);
   a.out = out;
   const dim3 grid((unsigned)(B * Hkv * a.S));
-  if (a.G <= 1)
-    hipLaunchKernelGGL(attn_decode_kernel<1>, grid, dim3(256), 0, s, a);
-  else if (a.G <= 2)
-    hipLaunchKernelGGL(attn_decode_kernel<2>, grid, dim3(256), 0, s, a);
-  else if (a.G <= 4)
-    hipLaunchKernelGGL(attn_decode_kernel<4>, grid, dim3(256), 0, s, a);
-  else if (a.G <= 8)
-    hipLaunchKernelGGL(attn_decode_kernel<8>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_decode_kernel<16>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_decode_kernel, grid, dim3(256), 0, s, a);
   int rc = hip_status(hipGetLastError());
   if (rc) return rc;
   const long long waves = (long long)B * Hq;

@@ -121,20 +121,35 @@ def test_k_page_matches_the_packed_weight_layout():
         assert pg[2048 + l] == s[l % 16, 0, l // 16]
 
 
-def test_v_page_pairs():
+def test_v_page_layout():
+    """V page bytes at hand-computed offsets: lane (d % 16) + 16 (r // 4),
+    byte 4 (d // 16) + r % 4 of its 32; scales at 2048 + 16 (r // 4) + 4 b + r % 4."""
     rng = np.random.default_rng(6)
     x = _bf16(rng, (5, 2, 128), 2.0)
     c, s = att.quantize_vectors(x)
     slots = np.array([3, 17, 18, 31, 40])
     pg = att.pack_pages(c, s, slots, 3, "v")
+    # (slot, dim) -> byte, worked out by hand
+    hand = {(3, 0): 32 * 0 + 0 + 3, (3, 17): 32 * 1 + 4 + 3, (1, 77): 32 * 13 + 16 + 1,
+            (2, 126): 32 * 14 + 28 + 2, (15, 127): 32 * 63 + 28 + 3, (8, 40): 32 * 40 + 8 + 0}
     for t, sl in enumerate(slots):
         p, r = divmod(int(sl), 16)
         for h in range(2):
-            for dim in (0, 1, 77, 126, 127):
-                assert pg[p, h, 32 * (dim // 2) + 2 * r + dim % 2] == c[t, h, dim]
+            for (rr, dim), off in hand.items():
+                if rr == r:
+                    assert pg[p, h, off] == c[t, h, dim]
+            for dim in range(128):
+                assert pg[p, h, 32 * (dim % 16 + 16 * (r // 4)) + 4 * (dim // 16) + r % 4] == c[t, h, dim]
             for b in range(4):
-                assert pg[p, h, 2048 + 16 * b + r] == s[t, h, b]
-    assert np.all(pg[2, :, 32 * 5 + 2 * 5] == 0)  # slot 37: never written
+                assert pg[p, h, 2048 + 16 * (r // 4) + 4 * b + r % 4] == s[t, h, b]
+    # slot 3, block 2 and slot 13, block 1, by hand
+    assert pg[0, 0, 2048 + 0 + 8 + 3] == s[0, 0, 2]
+    assert pg[2, 1, 2048 + 32 + 0 + 0] == s[4, 1, 0]  # slot 40 = page 2, slot 8, block 0
+    # slot 37 (page 2, slot 5) was never written
+    assert np.all(pg[2, :, [32 * (d % 16 + 16) + 4 * (d // 16) + 1 for d in range(128)]] == 0)
+    # every byte of a page is some (slot, dim) exactly once
+    seen = {32 * (d % 16 + 16 * (r // 4)) + 4 * (d // 16) + r % 4 for r in range(16) for d in range(128)}
+    assert seen == set(range(2048))
 
 
 def test_quantize_vectors_is_the_activation_quantizer():
