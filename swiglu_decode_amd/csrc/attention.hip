@@ -15,19 +15,21 @@
 //   V: lane l = (d % 16) + 16 (r / 4) holds 32 bytes, byte 4n + r % 4 the code
 //      of (slot r, dim 16n + d % 16): per 16-dim block n one dword of four
 //      consecutive slots, the operand order of a 16x16x16 bf16 matrix
-//      instruction's B operand (V as slots x dims); then byte
+//      instruction's A operand (V^T, dims x slots); then byte
 //      16 (r / 4) + 4b + r % 4 = the scale of (slot r, block b), the 16 bytes
 //      of one lane group together.
 //
 // Decode.  A workgroup takes one (sequence, KV head) and one of S splits of
 // the sequence's pages; its four wavefronts take every fourth page of the
 // split, RING pages in flight each.  Per page one 16x16x128 MX-scaled fp8
-// product gives the scores of all (up to 16) query heads of the group
-// against the page's 16 slots, the K tile being the shared operand (the
+// product gives the scores of the page's 16 slots against all (up to 16)
+// query heads of the group, the K tile being the shared operand (the
 // stride-0 broadcast); the online softmax (fp32, exp2, scores pre-multiplied
-// by sm_scale * log2 e) is updated once per RING pages; then o += p V on the
-// bf16 matrix instruction: V's E4M3 codes widened exactly to bf16, its
-// per-(slot, block) scale folded into p (rounded to bf16) by ldexp.
+// by sm_scale * log2 e) is updated once per RING pages; then o^T += V^T p^T
+// on the bf16 matrix instruction: V's E4M3 codes widened exactly to bf16,
+// its per-(slot, block) scale folded into p (rounded to bf16) by ldexp.  The
+// products are taken transposed so that p and the softmax rescale never
+// cross lanes through LDS.
 // The four wavefronts' states are merged in LDS into the split's partial
 // (row max, row sum, unnormalized o); a second kernel merges the splits and
 // writes bf16.  The work is HBM-bound: one pass over the sequence's K and V.
@@ -63,28 +65,6 @@ struct AttnArgs {
   uint16_t* out;       // [B, Hq, 128] bf16
 };
 
-
-// Max / sum over each row of 16 lanes, every lane of the row receiving the
-// result: lane exchanges within quads (swap neighbours, then pairs), then
-// the half-row and row mirrors (lane i with 7-i, then with 15-i), all
-// register moves between lanes (no LDS round trip).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<DPP_QUAD_XOR1>(v));
-  v = fmaxf(v, dpp<DPP_QUAD_XOR2>(v));
-  v = fmaxf(v, dpp<DPP_ROW_HALF_MIRROR>(v));
-  return fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<DPP_QUAD_XOR1>(v);
-  v += dpp<DPP_QUAD_XOR2>(v);
-  v += dpp<DPP_ROW_HALF_MIRROR>(v);
-  return v + dpp<DPP_ROW_MIRROR>(v);
-}
 
 // ---------------------------------------------------------------------------
 // cache write: one lane per (token, KV head, 32-dim block)
@@ -147,14 +127,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(int kind, const uint16_t*
 struct AttnLds {
   uint8_t qt[2048];           // the group's quantized queries as the A operand tile (rows >= G zero)
   uint8_t qs[64];             // their scale bytes, byte l = (head l % 16, block l / 16)
-  float p[4][MAXG][RING * PSLOTS];  // per wavefront: probabilities of the step's pages
-  float alpha[4][MAXG];       // per wavefront: rescale factors of the step
   float m[4][MAXG], l[4][MAXG];
   float o[4][MAXG][HD];
   int ids[MAXCHUNK];          // physical pages of this split
 };
 
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
+// (four wavefronts per SIMD: 118 registers, no spills; 3 per SIMD measured 5 % slower)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void attn_decode_kernel(AttnArgs a) {
   __shared__ AttnLds L;
   const int l = lane_id(), wv = (int)(threadIdx.x >> 6);
   const int S = a.S;
@@ -203,16 +182,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
                           *reinterpret_cast<const uint4*>(L.qt + 1024 + l * 16));
   const int qsc = L.qs[l];
 
-  // this wavefront's state: per head (row 4(l/16) + rr of the scores, held
-  // alike by the 16 lanes of a row group) the running max and sum; o as the
-  // matrix instruction's accumulators, 16-dim block n: heads 4(l/16) + rr,
-  // dim 16n + l % 16
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    mrow[rr] = -INFINITY;
-    lrow[rr] = 0.0f;
-  }
+  // Everything is computed transposed, so that no value crosses lanes
+  // through LDS: the scores as K Q^T (slots x heads), whose accumulator
+  // layout (lane l: head l % 16, slots 4(l/16)..+3) is the B operand layout
+  // of p^T in o^T = V^T p^T, and o^T's (lane l: head l % 16, dims
+  // 16n + 4(l/16) + rr) keeps each head's rescale in its own lanes.  Per lane:
+  // the running max and sum of head l % 16 (alike in its four lane groups).
+  const int q4 = 4 * (l >> 4);
+  float mh = -INFINITY, lh = 0.0f;
   v4f o[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -243,67 +220,59 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < RING; ++u) issue(u, p + 4 * u);
   for (; p < p1; p += 4 * RING) {
-    // the scores of the step's RING pages (heads 4(l/16)+rr against slot
-    // l%16 of page u, in log2 units), then one online-softmax update for all
-    // of them
-    v4f sc[RING];
+    // scores (log2 units) of the step's RING pages: slots 4(l/16)+j of page
+    // u against head l % 16; one online-softmax update for all of them
+    float sv[RING][4], mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
       const v4f z = {0.f, 0.f, 0.f, 0.f};
-      sc[u] = p + 4 * u < p1 ? mfma_f8(qa, R[u].k, z, qsc, (int)R[u].ks) : z;
-    }
+      const int pg = p + 4 * u;
+      const v4f sc = pg < p1 ? mfma_f8(R[u].k, qa, z, (int)R[u].ks, qsc) : z;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float sv[RING], mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < RING; ++u) {
-        const bool live = p + 4 * u < p1 && (p + 4 * u) * PSLOTS + (l & 15) < T;  // (this split's pages only)
-        sv[u] = live ? sc[u][rr] * a.qk_scale : -INFINITY;
-        mx = fmaxf(mx, sv[u]);
+      for (int j = 0; j < 4; ++j) {
+        const bool live = pg < p1 && pg * PSLOTS + q4 + j < T;  // (this split's pages only)
+        sv[u][j] = live ? sc[j] * a.qk_scale : -INFINITY;
+        mx = fmaxf(mx, sv[u][j]);
       }
-      mx = row16_max(mx);
-      const float mn = fmaxf(mrow[rr], mx);  // (finite: slot 0 of page p is live)
-      const float al = exp2f(mrow[rr] - mn);
-      float sm = 0.0f;
-      const int g = 4 * (l >> 4) + rr;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(mh, mx);  // (finite: slot 0 of page p is live)
+    const float al = exp2f(mh - mn);
+    float pr[RING][4], sm = 0.0f;
 #pragma unroll
-      for (int u = 0; u < RING; ++u) {
-        const float pr = sv[u] == -INFINITY ? 0.0f : exp2f(sv[u] - mn);
-        sm += pr;
-        L.p[wv][g][u * PSLOTS + (l & 15)] = pr;
+    for (int u = 0; u < RING; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pr[u][j] = sv[u][j] == -INFINITY ? 0.0f : exp2f(sv[u][j] - mn);
+        sm += pr[u][j];
       }
-      lrow[rr] = lrow[rr] * al + row16_sum(sm);
-      mrow[rr] = mn;
-      if ((l & 15) == 0) L.alpha[wv][g] = al;
-    }
-    // (LDS writes and reads of one wavefront complete in program order)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    {
-      const v4f al = *reinterpret_cast<const v4f*>(&L.alpha[wv][4 * (l >> 4)]);
+    sm += __shfl_xor(sm, 16, 64);
+    sm += __shfl_xor(sm, 32, 64);
+    lh = lh * al + sm;
+    mh = mn;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) o[n] *= al;
-    }
-    // o += p V page by page on the matrix unit: A = p (head l % 16, slots
-    // 4(l/16)..+3) times V's scale of (slot, 32-dim block), one operand per
-    // block; B = V's codes (slots 4(l/16)..+3, dim 16n + l % 16).  Slots past
-    // the length have p = 0 and zeroed codes (a stale slot may hold NaN
+    for (int n = 0; n < 8; ++n) o[n] *= al;
+    // o^T += V^T p^T page by page on the matrix unit: A = V's codes (dim
+    // 16n + l % 16, slots 4(l/16)..+3), B = p (head l % 16, the same slots)
+    // times V's scale of (slot, 32-dim block), one operand per block.  Slots
+    // past the length have p = 0 and zeroed codes (a stale slot may hold NaN
     // codes).  Each page's loads are reissued for the next step once used.
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
       const int pg = p + 4 * u;
       if (pg < p1) {
-        const v4f pp = *reinterpret_cast<const v4f*>(&L.p[wv][l & 15][u * PSLOTS + 4 * (l >> 4)]);
         const uint32_t vsw[4] = {R[u].vs.x, R[u].vs.y, R[u].vs.z, R[u].vs.w};
-        v4s pa[4];
+        v4s pb[4];
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
           v4bf t;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            t[j] = (__bf16)__builtin_amdgcn_ldexpf(pp[j], (int)((vsw[bk] >> (8 * j)) & 0xFFu) - 127);
-          pa[bk] = __builtin_bit_cast(v4s, t);
+            t[j] = (__bf16)__builtin_amdgcn_ldexpf(pr[u][j], (int)((vsw[bk] >> (8 * j)) & 0xFFu) - 127);
+          pb[bk] = __builtin_bit_cast(v4s, t);
         }
-        const int live = T - (pg * PSLOTS + 4 * (l >> 4));  // slots of this lane group within the length
+        const int live = T - (pg * PSLOTS + q4);  // slots of this lane group within the length
         const uint32_t keep = live >= 4 ? 0xFFFFFFFFu : live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - live)));
         const uint32_t vw[8] = {R[u].v0.x, R[u].v0.y, R[u].v0.z, R[u].v0.w, R[u].v1.x, R[u].v1.y, R[u].v1.z, R[u].v1.w};
 #pragma unroll
@@ -311,31 +280,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
           const uint32_t w = vw[n] & keep;
           const v2bf b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
           const v2bf b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-          const v4bf bv = {b0[0], b0[1], b1[0], b1[1]};
-          o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[n >> 1], __builtin_bit_cast(v4s, bv), o[n], 0, 0, 0);
+          const v4bf av = {b0[0], b0[1], b1[0], b1[1]};
+          o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, av), pb[n >> 1], o[n], 0, 0, 0);
         }
       }
       issue(u, pg + 4 * RING);
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
 
   // merge the four wavefronts into the split's partial
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int g = 4 * (l >> 4) + rr;
-    if ((l & 15) == 0) {
-      L.m[wv][g] = mrow[rr];
-      L.l[wv][g] = lrow[rr];
-    }
+  const int h = l & 15;
+  if (l < 16) {
+    L.m[wv][h] = mh;
+    L.l[wv][h] = lh;
   }
+  if (h < G) {
 #pragma unroll
-  for (int n = 0; n < 8; ++n)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int g = 4 * (l >> 4) + rr;
-      if (g < G) L.o[wv][g][16 * n + (l & 15)] = o[n][rr];
-    }
+    for (int n = 0; n < 8; ++n)
+      *reinterpret_cast<v4f*>(&L.o[wv][h][16 * n + q4]) = o[n];
+  }
   __syncthreads();
   float* part = a.part + (size_t)blockIdx.x * G * (2 + HD);
   for (int i = threadIdx.x; i < G * HD; i += 256) {
