@@ -313,6 +313,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
       acc += L.o[w][g][dd] * f;
       sum += L.l[w][g] * f;
     }
+    if (S == 1) {
+      // one split: the output itself (the merge kernel's arithmetic for a
+      // single partial; a sequence of length 0 gives zeros)
+      const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+      a.out[((size_t)b * a.Hq + (size_t)kvh * G + g) * HD + dd] = (uint16_t)f32_to_bf16(acc * inv);
+      continue;
+    }
     part[g * (2 + HD) + 2 + dd] = acc;
     if (dd == 0) {
       part[g * (2 + HD)] = M;
@@ -350,9 +357,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 }
 
 int attn_splits(int B, int Hkv, int max_pages) {
-  // enough workgroups to fill the GPU several times over, splits of at least
-  // 8 pages (128 tokens) and at most MAXCHUNK
-  int s = (2048 + B * Hkv - 1) / (B * Hkv);
+  // about 512 workgroups (two per compute unit; four fit, and every split
+  // adds a prologue, a merge and the second kernel: measured at batch 64 with
+  // 8 KV heads, 1 split 86 us, 2 splits 91-93, 4 splits 95-97, 8 splits 101),
+  // splits of at least 8 pages (128 tokens) and at most MAXCHUNK
+  int s = (512 + B * Hkv - 1) / (B * Hkv);
   const int by_len = (max_pages + 7) / 8;
   if (s > by_len) s = by_len;
   if (s > 64) s = 64;
@@ -399,7 +408,7 @@ int launch_paged_decode(const uint16_t* q, const uint8_t* kc, const uint8_t* vc,
   const dim3 grid((unsigned)(B * Hkv * a.S));
   hipLaunchKernelGGL(attn_decode_kernel, grid, dim3(256), 0, s, a);
   int rc = hip_status(hipGetLastError());
-  if (rc) return rc;
+  if (rc || a.S == 1) return rc;  // (one split: the decode kernel wrote the output)
   const long long waves = (long long)B * Hq;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
   return hip_status(hipGetLastError());
