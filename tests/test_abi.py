@@ -167,6 +167,33 @@ def test_argument_errors_launch_nothing(L):
     assert pa(q=0x1008) == E["EALIGN"]
     assert pa(bt=0x4002) == E["EALIGN"]
     assert pa(ws=wsa - 4) == E["EWORKSPACE"]
+    # large-M path: rows up to SGD_MAX_M_LARGE, offsets within 32 bits
+    w = _w(N=256, K=512)
+    lneed = L.sgd_gemm_large_workspace_bytes(BLK, 1000, 256, 512)
+    assert lneed > 256 * 1024
+    assert L.sgd_gemm_large_workspace_bytes(BLK, 65537, 256, 512) == 0
+    assert L.sgd_gemm_large_workspace_bytes(BLK, 65536, 256, 1 << 15) == 0  # 2^31 codes of Q(x)
+    assert L.sgd_gemm_large_workspace_bytes(3, 16, 256, 512) == 0
+    lg = lambda x=0x1000, M=1000, w_=w, y=0x2000, ws=0x10000, n=lneed: L.sgd_scaled_gemm_large(
+        P(x), M, ctypes.byref(w_), P(y), P(ws), n, None)
+    assert lg(M=0) == E["EINVAL"]
+    assert lg(M=65537) == E["EINVAL"]
+    assert lg(x=0) == E["EINVAL"]
+    assert lg(y=0x2008) == E["EALIGN"]
+    assert lg(ws=0) == E["EWORKSPACE"]
+    assert lg(ws=0x10008) == E["EALIGN"]
+    assert lg(n=lneed - 16) == E["EWORKSPACE"]
+    assert lg(w_=_w(fmt=9, N=256, K=512)) == E["EFMT"]
+    gu2, dn2 = _w(N=1024, K=256), _w(N=256, K=512)
+    pneed = L.sgd_mlp_prefill_workspace_bytes(BLK, 300, 256, 512)
+    assert pneed > lneed // 4
+    assert L.sgd_mlp_prefill_workspace_bytes(BLK, 300, 256, 40000) == 0
+    pf = lambda gu_=gu2, dn_=dn2, M=300, n=pneed: L.sgd_swiglu_mlp_prefill(
+        P(0x1000), M, ctypes.byref(gu_), ctypes.byref(dn_), P(0x2000), P(0x10000), n, None)
+    assert pf(dn_=_w(N=256, K=384)) == E["EDIM"]  # gate/up rows must be 2 ffn
+    assert pf(gu_=_w(fmt=MX, N=1024, K=256)) == E["EFMT"]
+    assert pf(M=0) == E["EINVAL"]
+    assert pf(n=pneed - 256) == E["EWORKSPACE"]
     # workspace status query: argument errors only (no GPU here)
     assert L.sgd_workspace_status(None, None) == E["EINVAL"]
     assert L.sgd_workspace_status(P(0x1004), None) == E["EALIGN"]

@@ -77,6 +77,24 @@ def test_decode_attention_parity(B, Hq, Hkv, lo, hi):
             assert rf <= 1e-2, (b, h, rf)
 
 
+@pytest.mark.parametrize("sm_scale", [0.02, 0.5])
+def test_decode_attention_custom_scale(sm_scale):
+    """A softmax scale other than 1/sqrt(head_dim): flat (0.02) and sharp
+    (0.5, a few tokens carry most of the weight) distributions."""
+    d = dev()
+    note(f"paged decode attention sm_scale={sm_scale}")
+    B, Hq, Hkv = 6, 16, 4
+    inp = synth.attention_inputs(B, Hq, Hkv, 1, 600, 2500, extra_pages=2)
+    kc, vc, _, _, _ = _build(inp, Hkv, d)
+    out = sgd.paged_decode_attention(inp["q"].to(d), kc, vc, inp["n_pages"], torch.from_numpy(inp["pages"]).to(d),
+                                     torch.from_numpy(inp["lens"]).to(d), Hkv, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    want = att.decode_attention(bf16_to_f64(inp["q"]), bf16_to_f64(inp["k"]), bf16_to_f64(inp["v"]), inp["lens"],
+                                sm_scale=sm_scale)
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert_close(got.reshape(B * Hq, -1), want.reshape(B * Hq, -1), f"decode attention sm_scale={sm_scale}")
+
+
 def test_decode_attention_edges():
     """A length of 0 gives zeros; a table entry outside the cache is harmless
     for the other sequences; a one-token sequence returns its dequantized V."""

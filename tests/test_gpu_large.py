@@ -140,6 +140,28 @@ def test_mlp_prefill_d4096_m1024_sampled_rows():
     assert_close(gpu_out_f64(y)[rows], ref.swiglu_mlp(bf16_to_f64(x[rows]), *q), "prefill MLP d4096 M=1024 rows")
 
 
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+def test_gemm_large_max_rows_sampled(fmt):
+    """The largest row count (SGD_MAX_M_LARGE = 65536): every output element
+    is written (the output starts as NaN) and nonzero rows come back, and 32
+    sampled rows, the last ones included, match the oracle."""
+    d = dev()
+    M, N, K = 65536, 256, 512
+    note(f"large GEMM {fmt} M={M} N={N} K={K} sampled rows")
+    x = synth.random_bf16((M, K), 950, 1.0)
+    w = synth.random_bf16((N, K), 951, 0.02)
+    pw = sgd.quantize_pack_weight(w.to(d), fmt)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=d)
+    sgd.scaled_gemm_large(x.to(d), pw, out=y)
+    torch.cuda.synchronize()
+    yc = gpu_out_f64(y)
+    assert np.all(np.isfinite(yc)) and np.all(np.abs(yc).max(axis=1) > 0)
+    rng = np.random.default_rng(952)
+    rows = np.concatenate([[0, M - 16, M - 1], rng.integers(0, M, 29)])
+    assert_close(yc[rows], ref.scaled_gemm(bf16_to_f64(x[rows]), oracle_weight(w, fmt)),
+                 f"large gemm {fmt} M={M} sampled rows")
+
+
 def test_large_path_keeps_control_block():
     """A large-path call on a workspace shared with the persistent kernels
     leaves their control block as they left it: the fused MLP still works
