@@ -52,6 +52,7 @@ namespace sgd {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
+
 // Per row-tile count MT (M rows padded to 16*MT): streaming wavefronts per
 // workgroup, ring depth (= k-tiles per chunk), LDS partial-sum slots.
 template <int MT>
@@ -75,6 +76,16 @@ struct Cfg {
   static constexpr bool KS = MT >= 4;
   static constexpr int PG = 8;
   static constexpr int DA = MT >= 8 ? 3 : 4;
+  // k-tiles of Q(x) the sync wavefront keeps in flight while staging
+  static constexpr int LD = MT >= 8 ? 4 : 2;
+  // Staged gate/up at 128-row tiles on the scaled fp8 matrix instruction
+  // instead of widening to bf16.  With one wavefront per SIMD the widening
+  // and the bf16 products (2,600 cycles per k-tile against 1,024 of matrix
+  // work) paced the loop as much as the staging did; fp8 products take a
+  // quarter of that.  Its coarser sums move the error against the oracle
+  // from 1.7e-3 to 2.2e-3 at 128 rows (the outlier widths do not stage).
+  // At 64 rows the widened bf16 path measured as fast, and stays.
+  static constexpr bool GU_F8 = MT >= 8;
 };
 
 // One LDS stage of staged gate/up activations: per m-tile the 2 KB operand
@@ -371,7 +382,7 @@ struct Streamer {
   }
 
   // ---- loads of one ring slot (unconditional: fillers read past the end) ----
-  template <bool GU, class Rg>
+  template <bool GU, class Rg, bool F8 = false>
   __device__ __forceinline__ void load_b(Rg& R, int s, const ChunkPos& cp, int KT, int k) {
     const int kt_ = cp.kt0 + k;
     const bool ok = cp.ok && kt_ < KT;
@@ -392,7 +403,7 @@ struct Streamer {
       const uint32_t KG = (uKT + 3u) >> 2;
       const uint32_t g0 = (n0 * KG + (kt >> 2)) * 256u;
       const uint32_t g1 = (n1 * KG + (kt >> 2)) * 256u;
-      if (GU) {
+      if (GU && !F8) {
         R.S0[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_gu0 : OOB, 0, 0);
         R.S1[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rs0, ok ? g0 + mo_gu1 : OOB, 0, 0);
         R.S0[s][1] = __builtin_amdgcn_raw_buffer_load_b32(rs1, ok ? g1 + mo_gu0 : OOB, 0, 0);
@@ -615,6 +626,35 @@ struct Streamer {
     }
   }
 
+  // Staged gate/up on the scaled fp8 matrix instruction (weights and Q(x)
+  // straight from their codes, MX scales in the instruction; block scales
+  // applied per k-tile as in step_dn).
+  template <class Rg>
+  __device__ __forceinline__ void step_gu_staged_f8(Rg& R, int s, int kt, const uint8_t* st, v4f (&acc)[2][MT]) {
+    const int l = lane_id();
+    const int sh = 8 * (kt & 3);
+    const uint8_t* sc = st + MT * 2048;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const v8i x = make_v8i(*reinterpret_cast<const uint4*>(st + mt * 2048 + l * 16),
+                             *reinterpret_cast<const uint4*>(st + mt * 2048 + 1024 + l * 16));
+      if (FMT == FMT_MX) {
+        const uint32_t e = reinterpret_cast<const uint32_t*>(sc)[mt * 16 + (l & 15)];
+        const int sa = (int)((e >> (8u * (uint32_t)(l >> 4))) & 0xFFu);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[nb][mt] = mfma_f8(x, R.RB[s][nb], acc[nb][mt], sa, (int)(R.S0[s][nb] >> sh));
+      } else {
+        const v4f xb = *reinterpret_cast<const v4f*>(sc + (16 * mt + 4 * (l >> 4)) * 4);
+        const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const v4f t = mfma_f8(x, R.RB[s][nb], z, 127, 127);
+          acc[nb][mt] += t * (xb * __uint_as_float(R.S0[s][nb]));
+        }
+      }
+    }
+  }
+
   // Staged gate/up for this wavefront's band (the q-th of the workgroup's
   // whole bands, if it has one): all k-tiles in order, the activations from
   // the LDS stages, then the band's SiLU, write-out and group accounting.
@@ -629,18 +669,19 @@ struct Streamer {
     const int KT = ph.KT;
     const uint32_t ep = launch_epoch(a);
     make_resources<PK_GU>();
+    constexpr bool F8 = Cfg<MT>::GU_F8;
     struct {
       v8i RB[PG][2];
       uint32_t S0[PG][2], S1[PG][2];
     } R;
     const ChunkPos cp{1, band, 0};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) load_b<true>(R, s, cp, KT, s);
+    for (int s = 0; s < 2; ++s) load_b<true, decltype(R), F8>(R, s, cp, KT, s);
     // the rest once Q(x) exists: a full prefetch at launch would delay the
     // x quantization and its cross-workgroup flags (measured)
     lds_wait_geq(gd, &L.xq_ok, 1u);
 #pragma unroll
-    for (int s = 2; s < PG; ++s) load_b<true>(R, s, cp, KT, s);
+    for (int s = 2; s < PG; ++s) load_b<true, decltype(R), F8>(R, s, cp, KT, s);
     v4f acc[2][MT];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
@@ -652,10 +693,13 @@ struct Streamer {
         const int kt = k0 + s;
         if (kt < KT) {
           lds_wait_geq(gd, &L.a_ready, (uint32_t)(kt + 1));
-          step_gu_staged(R, s, kt, stages + (kt % DA) * SB, acc);
+          if (F8)
+            step_gu_staged_f8(R, s, kt, stages + (kt % DA) * SB, acc);
+          else
+            step_gu_staged(R, s, kt, stages + (kt % DA) * SB, acc);
           if (lane_id() == 0) lds_store(&L.prog[q], (uint32_t)(kt + 1));
         }
-        load_b<true>(R, s, cp, KT, kt + PG);  // past K: a filler
+        load_b<true, decltype(R), F8>(R, s, cp, KT, kt + PG);  // past K: a filler
       }
     }
     finish_gu_band<MT, FMT>(a, band, acc, ep);
@@ -1287,7 +1331,7 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
 template <int MT, int FMT, int NS, int NSLOT>
 __device__ __forceinline__ void stage_activations(const Guard& gd, const Args& a, Lds<MT, NS, NSLOT>& L,
                                                   uint8_t* stages, int nst) {
-  constexpr int DA = Cfg<MT>::DA, SB = ks_stage_bytes<MT>(), LD = 2;
+  constexpr int DA = Cfg<MT>::DA, SB = ks_stage_bytes<MT>(), LD = Cfg<MT>::LD;
   const int l = lane_id();
   const uint32_t r = (uint32_t)(l & 15), g = (uint32_t)(l >> 4);
   const int KT = a.gu.KT;
