@@ -135,6 +135,7 @@ struct Args {
   void* as;                  // block fp32 [F/128][Mpad]; mx u8 [M][F/32]
   float* gpart;              // split-K partials of shared GU bands: [G][2 sides] slots
   float* dpart;              // split-K partials of shared DN bands: [G][2 sides] slots
+  float* amax;               // staged gate/up: [F/16][Mpad] each band's per-row max |a| over its 16 columns
   uint32_t scale_bytes_g, scale_bytes_2;  // packed weight-scale sizes
   int G;                     // workgroups in the grid
   int n_pairs, n_items;      // x quantization: (k-group, row tile) pairs, dealt into items
@@ -167,6 +168,8 @@ constexpr int CTRL_WORDS = 65536;
 constexpr size_t CTRL_BYTES = (size_t)CTRL_WORDS * 4;
 static_assert(CTRL_BYTES == CONTROL_BLOCK_BYTES, "control block size");
 constexpr int MAX_ITEMS = 512, MAX_GROUPS = 512, MAX_GBANDS = 2048;
+// staged gate/up: flag of band b (its row maxima are published), the last words
+constexpr int C_BFLAG = CTRL_WORDS - MAX_GBANDS;
 // Workgroups a grid may have; the workspace holds two partial-sum slots for each.
 constexpr int MAX_WG = 512;
 constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past every buffer's end
@@ -315,6 +318,9 @@ struct Ring {
 
 template <int MT, int FMT>
 __device__ void finish_gu_band(const Args& a, int b, v4f (&s)[2][MT], uint32_t ep);
+struct Guard;
+template <int MT, int FMT>
+__device__ void finish_gu_band_staged(const Args& a, int b, v4f (&s)[2][MT], uint32_t ep, const Guard& gd);
 
 template <int MT, int FMT, int P, int XL>
 struct Streamer {
@@ -702,7 +708,7 @@ struct Streamer {
         load_b<true, decltype(R), F8>(R, s, cp, KT, kt + PG);  // past K: a filler
       }
     }
-    finish_gu_band<MT, FMT>(a, band, acc, ep);
+    finish_gu_band_staged<MT, FMT>(a, band, acc, ep, gd);
   }
 
   // Wait until the groups of Q(a) that chunk cp reads are ready (its k-tiles
@@ -1278,6 +1284,121 @@ __device__ void finish_gu_band(const Args& a, int b, v4f (&s)[2][MT], uint32_t e
   raise_flag(a.ctrl, PG_RDY, grp, ep);
 }
 
+// End of band b of the staged gate/up, whose streaming wavefront owns the
+// whole band (so every band has an owner that reaches this point without
+// waiting on any other band).  The band re-quantizes its own 16 columns of
+// a = silu(g)*u from registers; the bands of one quantization block
+// exchange only their per-row maxima |a| (MX: the pair 2j, 2j+1 of a
+// 32-column block; block format: the 8 bands of a 128-column group).  The
+// codes and scales equal those of requant_group over the same fp32 values:
+// the block maximum does not depend on the order it is taken in, and each
+// code depends only on its value and the block's scale.  a itself is
+// stored afterwards, off the critical path, for inspection only.
+template <int MT, int FMT>
+__device__ void finish_gu_band_staged(const Args& a, int b, v4f (&s)[2][MT], uint32_t ep, const Guard& gd) {
+  const int l = lane_id(), c = l & 15, g4 = l >> 4;
+  float h[MT][4], am[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      h[mt][rr] = silu_mul(s[0][mt][rr], s[1][mt][rr]);
+      am[mt][rr] = fabsf(h[mt][rr]);
+    }
+  // row maxima over the band's 16 columns (the 16 lanes of a row group)
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) am[mt][rr] = fmaxf(am[mt][rr], __shfl_xor(am[mt][rr], off, WAVE));
+  // publish them (lane c < 4 of a row group: row 4*g4 + c), then the flag
+  float* amx = a.amax + (size_t)b * a.Mpad;
+  if (c < 4) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float v = c == 0 ? am[mt][0] : c == 1 ? am[mt][1] : c == 2 ? am[mt][2] : am[mt][3];
+      st_coherent(amx + mt * 16 + 4 * g4 + c, v);
+    }
+  }
+  drain_memory();
+  if (l == 0) store_agent(&a.ctrl[C_BFLAG + b], ep);
+  // the block's maxima: lane c reads band b0 + c % NB of its rows
+  constexpr int NB = FMT == FMT_MX ? 2 : 8;
+  const int b0 = b & ~(NB - 1);
+  wait_flags(gd, a.ctrl + C_BFLAG + b0, NB);
+  const float* src = a.amax + (size_t)(b0 + (c & (NB - 1))) * a.Mpad;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) am[mt][rr] = ld_coherent(src + mt * 16 + 4 * g4 + rr);
+#pragma unroll
+  for (int off = 1; off < NB; off <<= 1)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) am[mt][rr] = fmaxf(am[mt][rr], __shfl_xor(am[mt][rr], off, WAVE));
+  // codes of this band's 16 columns: lane (c, g4) codes rows 4*g4 + rr of
+  // column c; a 4x4 byte transpose within each lane quad gives lane
+  // 4j + i the codes of row 4*g4 + i, columns 4j..4j+3 (one dword)
+  const __amdgpu_buffer_rsrc_t raq = make_rsrc(a.aq, (uint32_t)a.M * (uint32_t)a.F);
+  const __amdgpu_buffer_rsrc_t ras =
+      make_rsrc(a.as, FMT == FMT_BLOCK ? (uint32_t)(a.F >> 7) * (uint32_t)a.Mpad * 4u : (uint32_t)a.M * (uint32_t)(a.F >> 5));
+  const int i = c & 3, quad = l & ~3;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    uint32_t d = 0, sv = 0;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float t;
+      if (FMT == FMT_BLOCK) {
+        const float sc = block_scale(am[mt][rr]);
+        t = h[mt][rr] / sc;
+        if (rr == i) sv = __float_as_uint(sc);
+      } else {
+        const int X = mx_exponent(am[mt][rr]);
+        t = h[mt][rr] * pow2_neg(X);
+        if (rr == i) sv = (uint32_t)(X + 127);
+      }
+      const float q = __builtin_amdgcn_fmed3f(t, -E4M3_MAX, E4M3_MAX);
+      d |= ((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xFFu) << (8 * rr);
+    }
+    uint32_t e = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e |= ((__shfl(d, quad + k, WAVE) >> (8 * i)) & 0xFFu) << (8 * k);
+    const int row = mt * 16 + 4 * g4 + i;
+    if (row < a.M) {
+      const uint32_t off = act_code_off(a.M, a.F, row, b * 16 + 4 * (c >> 2));
+      __builtin_amdgcn_raw_buffer_store_b32(e, raq, off, 0, AUX_SC1);
+      // the block's scale, once per row: lanes c < 4 of the band that writes it
+      if (c < 4) {
+        if (FMT == FMT_BLOCK) {
+          if ((b & 7) == 0) __builtin_amdgcn_raw_buffer_store_b32(sv, ras, ((uint32_t)(b >> 3) * (uint32_t)a.Mpad + (uint32_t)row) * 4u, 0, AUX_SC1);
+        } else if ((b & 1) == 0) {
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sv, ras, act_scale_off(a.M, a.F, row, b >> 3) + (uint32_t)((b >> 1) & 3), 0, AUX_SC1);
+        }
+      }
+    }
+  }
+  if (FMT == FMT_BLOCK && (b & 7) == 0) zero_pad_scales(static_cast<float*>(a.as) + (size_t)(b >> 3) * a.Mpad, a.M, a.Mpad);
+  drain_memory();
+  const int grp = b >> 3;
+  uint32_t old = 0;
+  if (l == 0) old = atomic_add_agent(&a.ctrl[C_GCNT + grp], 1u);
+  if (uni((int)old) == 7) {
+    if (l == 0) store_agent(&a.ctrl[C_GCNT + grp], 0u);  // (its last use in this launch)
+    raise_flag(a.ctrl, PG_RDY, grp, ep);
+  }
+  // a, for inspection (nothing in this launch reads it)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = mt * 16 + 4 * g4 + rr;
+      if (row < a.M) a.a32[(size_t)row * a.F + b * 16 + c] = h[mt][rr];
+    }
+}
+
 // BLK: the decode block's residual epilogue (h_out = h_in + bf16(y)); a
 // separate instantiation, so that the plain MLP carries none of its code.
 template <int MT, bool BLK>
@@ -1600,7 +1721,7 @@ struct Plan {
   int ks;  // staged gate/up
   int MT, Mpad, G, n_pairs, n_items, ngroups;
   Phase gu, dn;
-  size_t off_xa, off_xs, off_a32, off_aq, off_as, off_gpart, off_dpart, bytes;
+  size_t off_xa, off_xs, off_a32, off_aq, off_as, off_gpart, off_dpart, off_amax, bytes;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -1666,7 +1787,7 @@ Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp, int G) {
     p.ks = 1;
   }
   p.dn = make_phase(K2 / 128, N / 32, mlp ? cfg_pd(p.MT) : P, NS, G, false);
-  p.ok = p.ngroups <= MAX_GROUPS && (!mlp || F / 16 <= MAX_GBANDS) && N / 32 <= CTRL_WORDS - C_DPCNT;
+  p.ok = p.ngroups <= MAX_GROUPS && (!mlp || F / 16 <= MAX_GBANDS) && N / 32 <= C_BFLAG - C_DPCNT;
   size_t o = CTRL_BYTES;
   p.off_xa = o;
   o = align256(o + (size_t)M * K1);
@@ -1683,6 +1804,9 @@ Plan make_plan(int fmt, int M, int K1, int F, int N, int K2, bool mlp, int G) {
   if (mlp) o = align256(o + part);
   p.off_dpart = o;
   o = align256(o + part);
+  // (whether gate/up is staged depends on the grid; the layout does not)
+  p.off_amax = o;
+  if (mlp && p.MT >= 4) o = align256(o + (size_t)(F / 16) * p.Mpad * 4);
   p.bytes = o;
   return p;
 }
@@ -1905,6 +2029,7 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   a.as = ws + p.off_as;
   a.gpart = reinterpret_cast<float*>(ws + p.off_gpart);
   a.dpart = reinterpret_cast<float*>(ws + p.off_dpart);
+  a.amax = reinterpret_cast<float*>(ws + p.off_amax);
   a.G = G;
   a.n_pairs = p.n_pairs;
   a.n_items = XL ? 0 : p.n_items;
