@@ -77,15 +77,22 @@ struct Cfg {
   static constexpr int PG = 8;
   static constexpr int DA = MT >= 8 ? 3 : 4;
   // k-tiles of Q(x) the sync wavefront keeps in flight while staging
-  static constexpr int LD = MT >= 8 ? 4 : 2;
-  // Staged gate/up at 128-row tiles on the scaled fp8 matrix instruction
-  // instead of widening to bf16.  With one wavefront per SIMD the widening
-  // and the bf16 products (2,600 cycles per k-tile against 1,024 of matrix
-  // work) paced the loop as much as the staging did; fp8 products take a
-  // quarter of that.  Its coarser sums move the error against the oracle
-  // from 1.7e-3 to 2.2e-3 at 128 rows (the outlier widths do not stage).
-  // At 64 rows the widened bf16 path measured as fast, and stays.
-  static constexpr bool GU_F8 = MT >= 8;
+  static constexpr int LD = 4;
+  // Staged gate/up on the scaled fp8 matrix instruction instead of widening
+  // to bf16 (format FMT; see gu_f8).
+  template <int FMT>
+  static constexpr bool gu_f8() {
+    // With one wavefront per SIMD the widening and the bf16 products (2,600
+    // cycles per k-tile against 1,024 of matrix work at 128 rows) paced the
+    // loop as much as the staging did; fp8 products take a quarter of that.
+    // Their coarser sums move the error against the oracle from 1.7e-3 to
+    // 2.0-2.2e-3 at 64-128 rows.  Block-scaled weights at 64 rows (the
+    // 24-layer decode stack) keep the widened products: there the fp8 sums
+    // put the stack's logits outside the spread of equally valid results
+    // (depth 1: 1.9e-3 against 5.4e-4).  (The outlier widths, ffn = 13824,
+    // hold more bands than the staged schedule takes: bf16 path.)
+    return MT >= 8 || (MT >= 4 && FMT == FMT_MX);
+  }
 };
 
 // One LDS stage of staged gate/up activations: per m-tile the 2 KB operand
@@ -675,7 +682,7 @@ struct Streamer {
     const int KT = ph.KT;
     const uint32_t ep = launch_epoch(a);
     make_resources<PK_GU>();
-    constexpr bool F8 = Cfg<MT>::GU_F8;
+    constexpr bool F8 = Cfg<MT>::template gu_f8<FMT>();
     struct {
       v8i RB[PG][2];
       uint32_t S0[PG][2], S1[PG][2];
