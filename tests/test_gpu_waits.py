@@ -2,8 +2,9 @@
 persistent launches.
 
 * Give-up path: with a wait budget of 1 us set from the host, the waits of
-  the fused MLP (Q(x) readiness across workgroups for M > 32, Q(a) groups
-  before the second GEMM) outlive it; the kernel must still run to its end
+  the fused MLP (Q(x) readiness across workgroups for M > 32, the row
+  maxima the bands of a quantization block exchange in the staged schedule,
+  Q(a) groups before the second GEMM) outlive it; the kernel must still run to its end
   (the stream synchronises normally), the workspace must report
   SGD_ETIMEOUT, and after a clear a call at the normal budget must be right
   again.  No kernel is made to fault or hang: the condition is forced only
@@ -34,7 +35,9 @@ def _problem(d, ffn, fmt, M, seed, dv):
 
 def test_wait_budget_gives_up_and_every_kernel_exits():
     dv = dev()
-    cases = [(1024, 3072, "mx", 1), (1024, 3072, "block", 64), (2048, 6144, "block", 16)]
+    # (64 and 128 rows take the staged schedule: bands exchange their row
+    # maxima through flags of their own)
+    cases = [(1024, 3072, "mx", 1), (1024, 3072, "block", 64), (2048, 6144, "block", 16), (1024, 3072, "mx", 128)]
     statuses = []
     prev = sgd.set_wait_budget_us(1)
     try:
@@ -51,23 +54,23 @@ def test_wait_budget_gives_up_and_every_kernel_exits():
     assert all(s in (0, ETIMEOUT) for s in statuses), statuses
     assert ETIMEOUT in statuses, "no wait outlived a 1 us budget"
     # the workspace is usable again after a clear, at the normal budget
-    d, ffn, fmt, M = cases[0]
-    note(f"after give-up: clear and rerun {fmt} M={M}")
-    x, w, pws = _problem(d, ffn, fmt, M, 70 + M, dv)
-    ws = sgd.Workspace(dv, sgd.mlp_workspace_bytes(fmt, M, d, ffn))
-    prev = sgd.set_wait_budget_us(1)
-    try:
-        sgd.fused_swiglu_mlp(x.to(dv), *pws, workspace=ws)
+    for d, ffn, fmt, M in (cases[0], cases[3]):
+        note(f"after give-up: clear and rerun {fmt} M={M}")
+        x, w, pws = _problem(d, ffn, fmt, M, 70 + M, dv)
+        ws = sgd.Workspace(dv, sgd.mlp_workspace_bytes(fmt, M, d, ffn))
+        prev = sgd.set_wait_budget_us(1)
+        try:
+            sgd.fused_swiglu_mlp(x.to(dv), *pws, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            sgd.set_wait_budget_us(prev)
+        ws.clear()
+        assert ws.status() == 0
+        y = sgd.fused_swiglu_mlp(x.to(dv), *pws, workspace=ws)
         torch.cuda.synchronize()
-    finally:
-        sgd.set_wait_budget_us(prev)
-    ws.clear()
-    assert ws.status() == 0
-    y = sgd.fused_swiglu_mlp(x.to(dv), *pws, workspace=ws)
-    torch.cuda.synchronize()
-    assert ws.status() == 0
-    y_ref = ref.swiglu_mlp(bf16_to_f64(x), *(oracle_weight(t, fmt) for t in w))
-    assert_close(gpu_out_f64(y), y_ref, "after a give-up and a clear")
+        assert ws.status() == 0
+        y_ref = ref.swiglu_mlp(bf16_to_f64(x), *(oracle_weight(t, fmt) for t in w))
+        assert_close(gpu_out_f64(y), y_ref, f"after a give-up and a clear, {fmt} M={M}")
 
 
 def test_two_streams_default_workspace():
