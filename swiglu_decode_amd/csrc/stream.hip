@@ -1592,6 +1592,7 @@ __device__ __forceinline__ void sync_wave(const Args& a, Lds<MT, NS, NSLOT>& L, 
     // the launch number is about to wrap: clear every flag (flags of earlier
     // launches could otherwise match a later number)
     for (int i = l; i < NREP * PAGE_WORDS; i += 64) store_agent(&a.ctrl[PAGE0 + i], 0u);
+    for (int i = l; i < MAX_GBANDS; i += 64) store_agent(&a.ctrl[C_BFLAG + i], 0u);
     if (l == 0) store_agent(&a.ctrl[C_ERR_EP], 0u);
   }
   if (l == 0) {

@@ -162,7 +162,7 @@ def test_permuted_scales_are_caught(fmt):
 LAUNCH_COUNT_WORD = 64
 
 
-@pytest.mark.parametrize("fmt,M", [("mx", 4), ("block", 64)])
+@pytest.mark.parametrize("fmt,M", [("mx", 4), ("block", 64), ("mx", 128)])
 def test_launch_number_wrap(fmt, M):
     # preset the launch count just below 2**32 - 1: the calls then use launch
     # numbers 0xFFFFFFFE, 0xFFFFFFFF (which clears every flag on exit), 1, 2;
