@@ -145,8 +145,8 @@ int sgd_quantize_act(int fmt, const uint16_t* x_bf16, int M, int K,
 /* ---- workspaces -------------------------------------------------------- */
 /*
  * The GEMM and MLP kernels need a device workspace for the quantized
- * activations, the SwiGLU intermediate, split-K partial sums and
- * synchronisation counters.  Its first 256 KB are a control block that must
+ * activations, the SwiGLU intermediate, split-K partial sums, per-row maxima
+ * exchanged while re-quantizing (M > 32) and synchronisation counters.  Its first 256 KB are a control block that must
  * be zero-filled ONCE after allocation (sgd_workspace_clear or any fill
  * kernel); every call that completes leaves it ready for the next (counters
  * zero, flags holding the number of the launch that raised them), so one

@@ -123,8 +123,8 @@ def test_kernel_x_quantizer_bit_exact(fmt, M, d, xkind):
     _assert_scales_equal(mtile_scales(buf[off["xs"]:], M, d, fmt), s_ref, fmt, "Q(x) scales")
 
 
-REQ_CASES = [(1, 1024, 2048), (16, 1024, 2048), (17, 1024, 2048), (48, 1024, 2048), (64, 1024, 2048),
-             (100, 1024, 2048), (128, 1024, 2048),
+REQ_CASES = [(1, 1024, 2048), (16, 1024, 2048), (17, 1024, 2048), (33, 1024, 2048), (48, 1024, 2048),
+             (64, 1024, 2048), (100, 1024, 2048), (128, 1024, 2048),
              # shared gate/up bands (split-K combine) at one and two row tiles
              (1, 2560, 9728), (16, 2560, 9728), (32, 2560, 9728)]
 
