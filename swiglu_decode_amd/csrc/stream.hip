@@ -1643,10 +1643,10 @@ __global__ __launch_bounds__(64 * Cfg<MT>::NWAVE, 1) void stream_kernel(Args a) 
     int k = 0;
     XqLocal<FMT> xq;
     if (XL) {
-      // x first, through an empty memory pipeline: its latency is on the
-      // path to the first product, the weights' latency overlaps it
+      // x's loads first: the first product waits for them; the first weight
+      // slots go out right behind them (at 16 rows, 128 KB of x per
+      // workgroup, waiting for x before issuing them cost 0.5 us)
       xq.load(a);
-      drain_memory();
     }
     // the first weights are in flight while x is quantized
     auto quantize_x = [&]() {
