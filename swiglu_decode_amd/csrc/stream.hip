@@ -428,7 +428,7 @@ struct Streamer {
     }
   }
 
-  template <int PK, int PP>
+  template <int PK, int PP, int MLO = 0, int MHI = MT>
   __device__ __forceinline__ void load_a(Ring<MT, PP>& R, int s, const ChunkPos& cp, int KT, int k) {
     constexpr bool GU = PK == PK_GU;
     const int kt_ = cp.kt0 + k;
@@ -441,7 +441,7 @@ struct Streamer {
       const int rs = xl_row_stride(a.K1);
       const uint8_t* sc = lx + xl_scale_offset(16 * MT, a.K1);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = MLO; mt < MHI; ++mt) {
         const uint8_t* p = lx + (mt * 16 + (l & 15)) * rs + kt * 128 + 16 * (l >> 4);
         R.RA[s][mt] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
         if (FMT == FMT_BLOCK) {
@@ -457,7 +457,7 @@ struct Streamer {
     // whose row is past M read zeros
     const uint32_t r = (uint32_t)(lane_id() & 15), g = (uint32_t)(lane_id() >> 4);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = MLO; mt < MHI; ++mt) {
       const int Mt = min(16, a.M - 16 * mt);
       const bool v = ok && (int)r < Mt;
       const uint32_t uMt = (uint32_t)max(Mt, 0);
@@ -551,13 +551,13 @@ struct Streamer {
   }
 
   // Second GEMM: scaled fp8 MFMA (MX scales in the instruction).
-  template <int PP>
+  template <int PP, int MLO = 0, int MHI = MT>
   __device__ __forceinline__ void step_dn(Ring<MT, PP>& R, int s, int sa, int kt, v4f (&acc)[2][MT]) {
     const int sh = 8 * (kt & 3);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int mt = MLO; mt < MHI; ++mt) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int nb = 0; nb < 2; ++nb) {
         const v8i av = R.RA[sa][mt];
         if (FMT == FMT_BLOCK) {
           const v4f z = {0.f, 0.f, 0.f, 0.f};
@@ -568,6 +568,18 @@ struct Streamer {
         }
       }
     }
+  }
+
+  // Second GEMM, one ring slot: the matrix instructions of m-tile group g
+  // (NG groups), then that group's refill loads for the next chunk, so the
+  // refills go out while the matrix unit works through the rest
+  template <int PK, int PP, int G, int NG>
+  __device__ __forceinline__ void dn_slot(Ring<MT, PP>& R, int s, int kt, int KT, const ChunkPos& np,
+                                          v4f (&acc)[2][MT]) {
+    constexpr int LO = G * MT / NG, HI = (G + 1) * MT / NG;
+    if (kt < KT) step_dn<PP, LO, HI>(R, s, s, kt, acc);
+    load_a<PK, PP, LO, HI>(R, s, np, KT, s);
+    if constexpr (G + 1 < NG) dn_slot<PK, PP, G + 1, NG>(R, s, kt, KT, np, acc);
   }
 
   // Staged gate/up: the weights of band `band` at k-tile kt (ring slot s)
@@ -793,14 +805,19 @@ struct Streamer {
 #pragma unroll
         for (int s = 0; s < PP; ++s) {
           const int kt = cp.kt0 + s;
-          if (kt < KT) {
-            if (GU)
-              step_gu(R, s, s, kt, acc);
-            else
-              step_dn(R, s, s, kt, acc);
+          if (GU || MT < 4) {
+            if (kt < KT) {
+              if (GU)
+                step_gu(R, s, s, kt, acc);
+              else
+                step_dn(R, s, s, kt, acc);
+            }
+            load_b<GU>(R, s, np, KT, s);
+            load_a<PK>(R, s, np, KT, s);
+          } else {
+            dn_slot<PK, PP, 0, 2>(R, s, kt, KT, np, acc);
+            load_b<GU>(R, s, np, KT, s);
           }
-          load_b<GU>(R, s, np, KT, s);
-          load_a<PK>(R, s, np, KT, s);
         }
         c = cn;
         cp = np;
