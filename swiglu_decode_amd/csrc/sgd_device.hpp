@@ -223,4 +223,33 @@ __device__ __forceinline__ uint32_t ld_coherent_u32(__amdgpu_buffer_rsrc_t r, ui
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX_SC1);
 }
 
+// ---------------------------------------------------------------------------
+// Copies from memory straight into LDS (no register receives data).  Written
+// as the instructions themselves so that the compiler does not wait for them
+// before unrelated work; a kernel that uses them waits for its copies itself
+// (lds_copies_left: loads complete in issue order).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+// 1 KB: lane l's 16 bytes at buffer offset voff land at LDS byte m0 + 16*l.
+__device__ __forceinline__ void lds_copy1k(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+// 256 bytes: lane l's dword at buffer offset voff lands at LDS byte m0 + 4*l.
+__device__ __forceinline__ void lds_copy256(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+// As lds_copy256, agent-coherent (sc1): for small data other workgroups wrote.
+__device__ __forceinline__ void lds_copy256_sc1(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen sc1 lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+// Wait until at most N of this wavefront's memory loads are in flight.
+template <int N>
+__device__ __forceinline__ void lds_copies_left() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace sgd

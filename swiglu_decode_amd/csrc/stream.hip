@@ -61,7 +61,7 @@ struct Cfg {
   // (one row tile: 2 k-tiles per chunk measured 0.1-0.5 us faster than 4,
   // with fewer bytes queued in HBM ahead of each synchronisation)
   static constexpr int P = MT == 4 ? 4 : 2;
-  static constexpr int NSLOT = 2;
+  static constexpr int NSLOT = MT >= 8 ? 1 : 2;
   static constexpr int NWAVE = NS + 1;
   // ring slots (= k-tiles per chunk) of the MLP's second GEMM (deeper rings,
   // that would prefetch a workgroup's whole share of it while Q(a) is not
@@ -75,9 +75,10 @@ struct Cfg {
   // that all streaming wavefronts read.
   static constexpr bool KS = MT >= 4;
   static constexpr int PG = 8;
-  static constexpr int DA = MT >= 8 ? 3 : 4;
-  // k-tiles of Q(x) the sync wavefront keeps in flight while staging
-  static constexpr int LD = 4;
+  static constexpr int DA = 4;
+  // k-tiles of Q(x) the sync wavefront keeps in flight while staging (their
+  // copies within the 63 loads a wavefront can track, and fewer than DA)
+  static constexpr int LD = 3;
   // Staged gate/up on the scaled fp8 matrix instruction instead of widening
   // to bf16 (format FMT; see gu_f8).
   template <int FMT>
@@ -1471,12 +1472,20 @@ __device__ __forceinline__ void finish_dn_band(const Args& a, int b, v4f (&s)[2]
 
 // Staged gate/up: copy Q(x) (workspace, m-tile order) into the LDS stages
 // one k-tile at a time, for the nst streaming wavefronts that hold a band.
-// Stage kt % DA is rewritten once every one of them has used k-tile kt - DA;
-// LD k-tiles are in flight in registers.
+// The copies go from memory straight into LDS (2*MT 1 KB copies of codes and
+// MT/4 256-byte copies of row scales per k-tile, OPS in all), LD k-tiles in
+// flight; stage kt % DA is refilled once every one of those wavefronts has
+// used k-tile kt - DA.  No register holds the data, and this wavefront issues
+// no other loads meanwhile, so it waits for exactly the copies of the oldest
+// k-tile (register-held copies left the compiler waiting for nearly all of
+// them, which cut the staging to about one k-tile in flight).
 template <int MT, int FMT, int NS, int NSLOT>
 __device__ __forceinline__ void stage_activations(const Guard& gd, const Args& a, Lds<MT, NS, NSLOT>& L,
                                                   uint8_t* stages, int nst) {
   constexpr int DA = Cfg<MT>::DA, SB = ks_stage_bytes<MT>(), LD = Cfg<MT>::LD;
+  constexpr int NSC = (16 * MT + 63) / 64;  // 256-byte scale copies (one dword per row)
+  constexpr int OPS = 2 * MT + NSC;
+  static_assert(LD * OPS <= 63 && LD < DA, "copies in flight");
   const int l = lane_id();
   const uint32_t r = (uint32_t)(l & 15), g = (uint32_t)(l >> 4);
   const int KT = a.gu.KT;
@@ -1484,57 +1493,57 @@ __device__ __forceinline__ void stage_activations(const Guard& gd, const Args& a
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xa, (uint32_t)a.M * (uint32_t)a.K1);
   const __amdgpu_buffer_rsrc_t rxs =
       make_rsrc(a.xs, FMT == FMT_BLOCK ? KT1 * (uint32_t)a.Mpad * 4u : (uint32_t)a.M * (KT1 * 4u));
-  uint4 cb[LD][MT][2];
-  uint32_t sb[LD][2];
-  auto issue = [&](int u, int kt) {
-    const bool okk = kt < KT;
+  const uint32_t lds_st = lds_addr(stages);
+  auto copy = [&](int kt) {
+    const uint32_t base = lds_st + (uint32_t)((kt % DA) * SB);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int Mt = min(16, a.M - 16 * mt);
-      const bool v = okk && (int)r < Mt;
+      const bool v = (int)r < Mt;
       const uint32_t uMt = (uint32_t)max(Mt, 0);
       const uint32_t o = (uint32_t)mt * 16u * (uint32_t)a.K1 + ((uint32_t)kt * 8u + g) * 16u * uMt + r * 16u;
-      cb[u][mt][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, v ? o : OOB, 0, 0));
-      cb[u][mt][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, v ? o + 64u * uMt : OOB, 0, 0));
+      lds_copy1k(rx, base + (uint32_t)(mt * 2048), v ? o : OOB);
+      lds_copy1k(rx, base + (uint32_t)(mt * 2048 + 1024), v ? o + 64u * uMt : OOB);
     }
+    // entry e (row e % 16 of m-tile e / 16): lane l of copy j carries e = 64 j + l
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = 2 * l + j;  // row e % 16 of m-tile e / 16 (16*MT entries: lanes < 8*MT)
+    for (int j = 0; j < NSC; ++j) {
+      const int e = 64 * j + l;
       uint32_t off = OOB;
       if (e >= 16 * MT) {
       } else if (FMT == FMT_BLOCK) {
-        if (okk) off = ((uint32_t)kt * (uint32_t)a.Mpad + (uint32_t)e) * 4u;
+        off = ((uint32_t)kt * (uint32_t)a.Mpad + (uint32_t)e) * 4u;
       } else {
         const int mt = e >> 4, rr = e & 15;
         const int Mt = min(16, a.M - 16 * mt);
-        if (okk && rr < Mt)
-          off = (uint32_t)mt * 16u * KT1 * 4u + (uint32_t)kt * 4u * (uint32_t)Mt + (uint32_t)rr * 4u;
+        if (rr < Mt) off = (uint32_t)mt * 16u * KT1 * 4u + (uint32_t)kt * 4u * (uint32_t)Mt + (uint32_t)rr * 4u;
       }
-      sb[u][j] = ld_coherent_u32(rxs, off);
+      lds_copy256_sc1(rxs, base + (uint32_t)(MT * 2048 + 256 * j), off);
     }
   };
-  auto write = [&](int u, int kt) {
-    uint8_t* st = stages + (kt % DA) * SB;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      *reinterpret_cast<uint4*>(st + mt * 2048 + l * 16) = cb[u][mt][0];
-      *reinterpret_cast<uint4*>(st + mt * 2048 + 1024 + l * 16) = cb[u][mt][1];
-    }
-    if (l < 8 * MT) *reinterpret_cast<uint2*>(st + MT * 2048 + l * 8) = make_uint2(sb[u][0], sb[u][1]);
+  auto stage_free = [&](int kt) {
+    if (kt >= DA)
+      for (int w = 0; w < nst; ++w) lds_wait_geq(gd, &L.prog[w], (uint32_t)(kt - DA + 1));
   };
-#pragma unroll
-  for (int u = 0; u < LD; ++u) issue(u, u);
-  for (int k0 = 0; k0 < KT; k0 += LD) {
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int kt = k0 + u;
-      if (kt < KT) {
-        if (kt >= DA)
-          for (int w = 0; w < nst; ++w) lds_wait_geq(gd, &L.prog[w], (uint32_t)(kt - DA + 1));
-        write(u, kt);
-        if (l == 0) lds_store(&L.a_ready, (uint32_t)(kt + 1));
-      }
-      issue(u, kt + LD);
+  for (int t = 0; t < LD && t < KT; ++t) {
+    stage_free(t);
+    copy(t);
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    // copies issued after k-tile kt's: those of the next min(LD - 1, KT - 1 - kt) k-tiles
+    const int after = min(LD - 1, KT - 1 - kt);
+    if (after >= 3)
+      lds_copies_left<(LD >= 4 ? 3 : 0) * OPS>();
+    else if (after == 2)
+      lds_copies_left<(LD >= 3 ? 2 : 0) * OPS>();
+    else if (after == 1)
+      lds_copies_left<OPS>();
+    else
+      lds_copies_left<0>();
+    if (l == 0) lds_store(&L.a_ready, (uint32_t)(kt + 1));
+    if (kt + LD < KT) {
+      stage_free(kt + LD);
+      copy(kt + LD);
     }
   }
 }

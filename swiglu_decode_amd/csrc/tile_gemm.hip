@@ -49,30 +49,7 @@ struct TileArgs {
   int tiles_m;       // blocks along M (the grid is tiles_m x blocks along N)
 };
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ int uni_t(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// 1 KB from memory straight into LDS: lane l's 16 bytes at buffer offset
-// voff land at LDS byte m0 + 16*l.  Written as the instruction itself so that
-// the compiler does not wait for it before unrelated LDS reads; the kernel
-// waits for these copies itself (lds_copies_left) before its barrier.  No
-// register receives data.
-__device__ __forceinline__ void lds_copy1k(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
-}
-
-// 256 bytes from memory straight into LDS: lane l's dword at buffer offset
-// voff lands at LDS byte m0 + 4*l (the scales of a stage).
-__device__ __forceinline__ void lds_copy256(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
-}
-// Wait until at most N of this wavefront's memory loads are in flight (loads
-// complete in issue order, so every copy issued before the last N is done).
-template <int N>
-__device__ __forceinline__ void lds_copies_left() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // LDS stage of the tiled GEMM: the k-tile's AT activation tiles and BT weight
 // tiles (2 KB each, A first), then the scales: 64 bytes per m-tile (mx: the
