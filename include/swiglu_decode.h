@@ -182,7 +182,8 @@ size_t sgd_mlp_workspace_bytes(int fmt, int M, int d, int ffn);
  * zero).  MX32 scales: m-tile t holds, per 128-column k-tile, the Mt rows'
  * four E8M0 bytes (one dword per row, 32-column blocks in order).  Q(x) is
  * written to the workspace only when it does not fit in LDS (in practice
- * M > 32, or a very wide d); a, Q(a) always.  Returns SGD_OK or
+ * M > 32, or a very wide d); Q(a) always; a always at M <= 32 and otherwise
+ * only with sgd_set_keep_intermediates(1).  Returns SGD_OK or
  * SGD_EINVAL (shape or format invalid, or offsets NULL).
  */
 int sgd_mlp_workspace_layout(int fmt, int M, int d, int ffn, size_t* offsets);
@@ -197,6 +198,15 @@ int sgd_workspace_clear(void* workspace, size_t bytes, void* stream);
  * when a call is launched (a captured graph keeps the value of its capture).
  * Returns the previous budget. */
 uint32_t sgd_set_wait_budget_us(uint32_t us);
+
+/* Keep the SwiGLU intermediate for inspection: when nonzero, fused MLP and
+ * decode-block calls also store a = silu(g)*u (fp32) in the workspace where
+ * sgd_mlp_workspace_layout says, also on the path (M > 32) whose re-
+ * quantization works from registers and does not otherwise store it.  For
+ * tests and debugging; it costs store bandwidth.  Process-wide, read when a
+ * call is launched (a captured graph keeps the value of its capture); 0 by
+ * default.  Returns the previous setting. */
+int sgd_set_keep_intermediates(int keep);
 
 /* Whether any launch on `workspace` gave up a wait since the workspace was
  * last cleared: SGD_OK, or SGD_ETIMEOUT (then the outputs of the call(s)

@@ -20,7 +20,7 @@ __all__ = [
     "fmt_code", "quantize_pack_weight", "unpack_weight", "quantize_act", "scaled_gemm",
     "fused_swiglu_mlp", "bf16_to_f32", "rmsnorm_bf16", "residual_add", "head_logits",
     "argmax_rows", "gemm_workspace_bytes", "mlp_workspace_bytes", "lib",
-    "workspace_status", "set_wait_budget_us", "mlp_workspace_layout", "fused_swiglu_mlp_noalloc",
+    "workspace_status", "set_wait_budget_us", "set_keep_intermediates", "mlp_workspace_layout", "fused_swiglu_mlp_noalloc",
     "scaled_gemm_f32", "swiglu_quantize", "scaled_gemm_q", "stack_packed", "unfused_swiglu_mlp",
 ]
 
@@ -221,6 +221,13 @@ def set_wait_budget_us(us):
     """Set the persistent kernels' wait budget in microseconds (0: default
     1 s); returns the previous value.  Process-wide."""
     return int(lib().sgd_set_wait_budget_us(int(us)))
+
+
+def set_keep_intermediates(keep):
+    """Also store a = silu(g)*u in the workspace on the path that does not
+    need it (M > 32), for inspection; returns the previous setting.
+    Process-wide."""
+    return int(lib().sgd_set_keep_intermediates(1 if keep else 0))
 
 
 def mlp_workspace_layout(fmt, M, d, ffn):

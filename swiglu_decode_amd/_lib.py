@@ -70,6 +70,7 @@ SIGNATURES = {
     "sgd_argmax_rows": (_i, [_vp, _i, _i, _vp, _vp]),
     "sgd_read_stream": (_i, [_vp, _sz, _vp, _vp]),
     "sgd_set_wait_budget_us": (ctypes.c_uint32, [ctypes.c_uint32]),
+    "sgd_set_keep_intermediates": (ctypes.c_int, [ctypes.c_int]),
     "sgd_workspace_status": (_i, [_vp, _vp]),
     "sgd_mlp_workspace_layout": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
 }

@@ -19,6 +19,8 @@ constexpr size_t MAX_WEIGHT_BYTES = size_t(1) << 31;
 // The persistent kernels' wait budget (sgd_set_wait_budget_us).
 constexpr uint32_t DEFAULT_WAIT_BUDGET_US = 1000000;
 std::atomic<uint32_t> g_wait_budget_us{DEFAULT_WAIT_BUDGET_US};
+// Whether fused calls keep a = silu(g)*u in the workspace (sgd_set_keep_intermediates).
+std::atomic<int> g_keep_intermediates{0};
 
 inline bool fmt_ok(int fmt) { return fmt == SGD_FMT_BLOCK128 || fmt == SGD_FMT_MX32; }
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -49,6 +51,7 @@ int check_weight(const sgd_weight* w) {
 
 namespace sgd {
 uint64_t wait_budget_ticks() { return (uint64_t)g_wait_budget_us.load(std::memory_order_relaxed) * 100u; }
+bool keep_intermediates() { return g_keep_intermediates.load(std::memory_order_relaxed) != 0; }
 
 int check_mlp_args(const uint16_t* x_bf16, int M, const sgd_weight* gate, const sgd_weight* up,
                    const sgd_weight* down, const uint16_t* y_bf16) {
@@ -150,6 +153,8 @@ int sgd_workspace_clear(void* workspace, size_t bytes, void* stream) {
   if (!al16(workspace) || (bytes % 16)) return SGD_EALIGN;
   return launch_fill_zero(workspace, bytes, as_stream(stream));
 }
+
+int sgd_set_keep_intermediates(int keep) { return g_keep_intermediates.exchange(keep ? 1 : 0, std::memory_order_relaxed); }
 
 uint32_t sgd_set_wait_budget_us(uint32_t us) {
   return g_wait_budget_us.exchange(us == 0 ? DEFAULT_WAIT_BUDGET_US : us, std::memory_order_relaxed);

@@ -90,6 +90,9 @@ constexpr int CTRL_ERR_WORD = 65;
 // the launch gives up (sgd_set_wait_budget_us), in ticks of the device's
 // 100 MHz real-time counter.
 uint64_t wait_budget_ticks();
+// Whether fused calls also store a = silu(g)*u where their path does not
+// need it (sgd_set_keep_intermediates).
+bool keep_intermediates();
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? SGD_OK : SGD_EHIP; }
 

@@ -149,6 +149,7 @@ struct Args {
   int n_pairs, n_items;      // x quantization: (k-group, row tile) pairs, dealt into items
   int ngroups;               // F / 128
   int ks;                    // gate/up with LDS-staged activations (Cfg::KS variants)
+  int keep_a;                // staged gate/up: also store a for inspection
   uint64_t budget;           // longest a wait may spin, in ticks of the 100 MHz real-time counter
   Phase gu, dn;
 };
@@ -1414,14 +1415,16 @@ __device__ void finish_gu_band_staged(const Args& a, int b, v4f (&s)[2][MT], uin
     if (l == 0) store_agent(&a.ctrl[C_GCNT + grp], 0u);  // (its last use in this launch)
     raise_flag(a.ctrl, PG_RDY, grp, ep);
   }
-  // a, for inspection (nothing in this launch reads it)
+  // a, for inspection only (nothing in this launch reads it)
+  if (a.keep_a) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = mt * 16 + 4 * g4 + rr;
-      if (row < a.M) a.a32[(size_t)row * a.F + b * 16 + c] = h[mt][rr];
-    }
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = mt * 16 + 4 * g4 + rr;
+        if (row < a.M) a.a32[(size_t)row * a.F + b * 16 + c] = h[mt][rr];
+      }
+  }
 }
 
 // BLK: the decode block's residual epilogue (h_out = h_in + bf16(y)); a
@@ -2086,6 +2089,7 @@ int launch_stream(const Problem& pr, hipStream_t s) {
   }
   a.ngroups = p.ngroups;
   a.ks = p.ks;
+  a.keep_a = keep_intermediates() ? 1 : 0;
   a.budget = wait_budget_ticks();
   a.gu = p.gu;
   a.dn = p.dn;

@@ -223,6 +223,14 @@ def test_wait_budget_setting(L):
     L.sgd_set_wait_budget_us(0)
 
 
+def test_keep_intermediates_setting(L):
+    # process-wide, off by default; any nonzero value reads back as 1
+    prev = L.sgd_set_keep_intermediates(7)
+    assert prev == 0
+    assert L.sgd_set_keep_intermediates(0) == 1
+    assert L.sgd_set_keep_intermediates(0) == 0
+
+
 def test_binding_refuses_wrong_dtypes_without_gpu():
     import torch
     import swiglu_decode_amd as sgd

@@ -138,7 +138,13 @@ def test_kernel_requant_bit_exact(fmt, M, d, ffn):
     w = _weights(d, ffn, fmt, 500 + d)
     pws = [sgd.quantize_pack_weight(t.to(dv), fmt) for t in w]
     ws = sgd.Workspace(dv, sgd.mlp_workspace_bytes(fmt, M, d, ffn))
-    _, off, buf = _run(x, pws, fmt, M, d, ffn, ws)
+    # (a is kept in the workspace for this check: above 32 rows the kernel
+    # re-quantizes from registers and stores a only when asked to)
+    prev = sgd.set_keep_intermediates(True)
+    try:
+        _, off, buf = _run(x, pws, fmt, M, d, ffn, ws)
+    finally:
+        sgd.set_keep_intermediates(prev)
     a_gpu = buf[off["a"]:off["a"] + M * ffn * 4].view(np.float32).reshape(M, ffn).astype(np.float64)
     # the product itself, against the oracle's fp64 one (fp32 accumulation)
     q = [oracle_weight(t, fmt) for t in w]
