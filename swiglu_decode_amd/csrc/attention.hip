@@ -20,13 +20,14 @@
 //      of one lane group together.
 //
 // Decode.  A workgroup takes one (sequence, KV head) and one of S splits of
-// the sequence's pages; its four wavefronts take every fourth page of the
-// split, RING pages in flight each.  Per page one 16x16x128 MX-scaled fp8
-// product gives the scores of the page's 16 slots against all (up to 16)
-// query heads of the group, the K tile being the shared operand (the
-// stride-0 broadcast); the online softmax (fp32, exp2, scores pre-multiplied
-// by sm_scale * log2 e) is updated once per RING pages; then o^T += V^T p^T
-// on the bf16 matrix instruction: V's E4M3 codes widened exactly to bf16,
+// the sequence's pages (with one split, workgroups are matched to pairs in
+// order of length, so that the compute units get similar shares); its four
+// wavefronts take every fourth page of the split, RING pages in flight each.
+// Per page one 16x16x128 MX-scaled fp8 product gives the scores of the
+// page's 16 slots against all (up to 16) query heads of the group, the K
+// tile being the shared operand (the stride-0 broadcast); the online softmax
+// (fp32, exp2, scores pre-multiplied by sm_scale * log2 e) is updated; then
+// o^T += V^T p^T on the bf16 matrix instruction: V's E4M3 codes widened exactly to bf16,
 // its per-(slot, block) scale folded into p (rounded to bf16) by ldexp.  The
 // products are taken transposed so that p and the softmax rescale never
 // cross lanes through LDS.
@@ -45,7 +46,8 @@ constexpr int HD = 128;               // head_dim
 constexpr int PSLOTS = 16;            // token slots per page
 constexpr int PAGE_BYTES = 2112;      // per (page, KV head)
 constexpr int MAXG = 16;              // query heads per KV head
-constexpr int RING = 2;               // pages in flight per wavefront (4 and 8 measured slower: fewer wavefronts fit)
+constexpr int RING = 2;               // pages in flight per wavefront (3, 4 and 6 measured no faster)
+constexpr int MAXB_ORDER = 256;      // batches up to this size take workgroups in order of length
 constexpr int MAXCHUNK = 1024;        // pages of one split (their ids are staged in LDS)
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -130,6 +132,7 @@ struct AttnLds {
   float m[4][MAXG], l[4][MAXG];
   float o[4][MAXG][HD];
   int ids[MAXCHUNK];          // physical pages of this split
+  int len[256];               // sequence lengths (for the work order)
 };
 
 // (four wavefronts per SIMD: 118 registers, no spills; 3 per SIMD measured 5 % slower)
@@ -137,11 +140,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
   __shared__ AttnLds L;
   const int l = lane_id(), wv = (int)(threadIdx.x >> 6);
   const int S = a.S;
-  const int split = blockIdx.x % S, bh = blockIdx.x / S;
+  const int split = blockIdx.x % S;
+  int bh = blockIdx.x / S;
+  const int Tmax = a.max_pages * PSLOTS;
+  if (S == 1 && a.B <= MAXB_ORDER) {
+    // Work order by length: workgroup w < half takes the w-th longest
+    // (sequence, KV head) pair and workgroup half + w the w-th shortest.
+    // When every workgroup is resident, w and half + w tend to share a
+    // compute unit, which then holds about twice the mean length.
+    for (int t = threadIdx.x; t < a.B; t += 256) {
+      const int v = a.lens[t];
+      L.len[t] = v < 0 ? 0 : (v > Tmax ? Tmax : v);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.B; t += 256) {
+      const int lt = L.len[t];
+      int rank = 0;
+      for (int u = 0; u < a.B; ++u) rank += (L.len[u] > lt || (L.len[u] == lt && u < t)) ? 1 : 0;
+      L.ids[rank] = t;  // (sequences by length, longest first; ties by index)
+    }
+    __syncthreads();
+    const int n = a.B * a.Hkv, half = (n + 1) / 2;
+    const int r = bh < half ? bh : n - 1 - (bh - half);
+    bh = L.ids[r / a.Hkv] * a.Hkv + r % a.Hkv;
+    __syncthreads();  // (the page ids below overwrite the order)
+  }
   const int b = bh / a.Hkv, kvh = bh - b * a.Hkv;
   const int G = a.G;
   int T = a.lens[b];
-  T = T < 0 ? 0 : (T > a.max_pages * PSLOTS ? a.max_pages * PSLOTS : T);
+  T = T < 0 ? 0 : (T > Tmax ? Tmax : T);
   const int npages = (T + PSLOTS - 1) / PSLOTS;
   const int p0 = split * a.chunk, p1 = min(npages, p0 + a.chunk);
 
@@ -216,74 +243,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     R[u].v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + l * 32 + 16 : base, 0, AUX_NT));
     R[u].vs = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, in ? base + 2048 + 16 * (l >> 4) : base, 0, 0));  // (this lane group's slots)
   };
-  int p = p0 + wv;
+  // Each page is taken on its own: its scores, one online-softmax update,
+  // then o^T += V^T p^T; its slot is refilled with the page RING steps ahead
+  // right after, so the loads of the next RING - 1 pages stay in flight
+  // while a page is worked on.
+  auto page_step = [&](int u, int pg) {
+    // scores (log2 units): slots 4(l/16)+j of page pg against head l % 16
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    const v4f sc = mfma_f8(R[u].k, qa, z, (int)R[u].ks, qsc);
+    float sv[4], mx = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < RING; ++u) issue(u, p + 4 * u);
-  for (; p < p1; p += 4 * RING) {
-    // scores (log2 units) of the step's RING pages: slots 4(l/16)+j of page
-    // u against head l % 16; one online-softmax update for all of them
-    float sv[RING][4], mx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < RING; ++u) {
-      const v4f z = {0.f, 0.f, 0.f, 0.f};
-      const int pg = p + 4 * u;
-      const v4f sc = pg < p1 ? mfma_f8(R[u].k, qa, z, (int)R[u].ks, qsc) : z;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool live = pg < p1 && pg * PSLOTS + q4 + j < T;  // (this split's pages only)
-        sv[u][j] = live ? sc[j] * a.qk_scale : -INFINITY;
-        mx = fmaxf(mx, sv[u][j]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const bool live = pg * PSLOTS + q4 + j < T;
+      sv[j] = live ? sc[j] * a.qk_scale : -INFINITY;
+      mx = fmaxf(mx, sv[j]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(mh, mx);  // (finite: slot 0 of page p is live)
+    const float mn = fmaxf(mh, mx);  // (finite: slot 0 of the page is live)
     const float al = exp2f(mh - mn);
-    float pr[RING][4], sm = 0.0f;
+    float pr[4], sm = 0.0f;
 #pragma unroll
-    for (int u = 0; u < RING; ++u)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pr[u][j] = sv[u][j] == -INFINITY ? 0.0f : exp2f(sv[u][j] - mn);
-        sm += pr[u][j];
-      }
+    for (int j = 0; j < 4; ++j) {
+      pr[j] = sv[j] == -INFINITY ? 0.0f : exp2f(sv[j] - mn);
+      sm += pr[j];
+    }
     sm += __shfl_xor(sm, 16, 64);
     sm += __shfl_xor(sm, 32, 64);
     lh = lh * al + sm;
     mh = mn;
 #pragma unroll
     for (int n = 0; n < 8; ++n) o[n] *= al;
-    // o^T += V^T p^T page by page on the matrix unit: A = V's codes (dim
-    // 16n + l % 16, slots 4(l/16)..+3), B = p (head l % 16, the same slots)
-    // times V's scale of (slot, 32-dim block), one operand per block.  Slots
-    // past the length have p = 0 and zeroed codes (a stale slot may hold NaN
-    // codes).  Each page's loads are reissued for the next step once used.
+    // o^T += V^T p^T on the matrix unit: A = V's codes (dim 16n + l % 16,
+    // slots 4(l/16)..+3), B = p (head l % 16, the same slots) times V's
+    // scale of (slot, 32-dim block), one operand per block.  Slots past the
+    // length have p = 0 and zeroed codes (a stale slot may hold NaN codes).
+    const uint32_t vsw[4] = {R[u].vs.x, R[u].vs.y, R[u].vs.z, R[u].vs.w};
+    v4s pb[4];
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      v4bf t;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[j] = (__bf16)__builtin_amdgcn_ldexpf(pr[j], (int)((vsw[bk] >> (8 * j)) & 0xFFu) - 127);
+      pb[bk] = __builtin_bit_cast(v4s, t);
+    }
+    const int live = T - (pg * PSLOTS + q4);  // slots of this lane group within the length
+    const uint32_t keep = live >= 4 ? 0xFFFFFFFFu : live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - live)));
+    const uint32_t vw[8] = {R[u].v0.x, R[u].v0.y, R[u].v0.z, R[u].v0.w, R[u].v1.x, R[u].v1.y, R[u].v1.z, R[u].v1.w};
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const uint32_t w = vw[n] & keep;
+      const v2bf b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+      const v2bf b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+      const v4bf av = {b0[0], b0[1], b1[0], b1[1]};
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, av), pb[n >> 1], o[n], 0, 0, 0);
+    }
+  };
+  int p = p0 + wv;
+#pragma unroll
+  for (int u = 0; u < RING; ++u) issue(u, p + 4 * u);
+  for (; p < p1; p += 4 * RING) {
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
       const int pg = p + 4 * u;
-      if (pg < p1) {
-        const uint32_t vsw[4] = {R[u].vs.x, R[u].vs.y, R[u].vs.z, R[u].vs.w};
-        v4s pb[4];
-#pragma unroll
-        for (int bk = 0; bk < 4; ++bk) {
-          v4bf t;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            t[j] = (__bf16)__builtin_amdgcn_ldexpf(pr[u][j], (int)((vsw[bk] >> (8 * j)) & 0xFFu) - 127);
-          pb[bk] = __builtin_bit_cast(v4s, t);
-        }
-        const int live = T - (pg * PSLOTS + q4);  // slots of this lane group within the length
-        const uint32_t keep = live >= 4 ? 0xFFFFFFFFu : live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - live)));
-        const uint32_t vw[8] = {R[u].v0.x, R[u].v0.y, R[u].v0.z, R[u].v0.w, R[u].v1.x, R[u].v1.y, R[u].v1.z, R[u].v1.w};
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const uint32_t w = vw[n] & keep;
-          const v2bf b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-          const v2bf b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-          const v4bf av = {b0[0], b0[1], b1[0], b1[1]};
-          o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, av), pb[n >> 1], o[n], 0, 0, 0);
-        }
-      }
+      if (pg < p1) page_step(u, pg);
       issue(u, pg + 4 * RING);
     }
   }

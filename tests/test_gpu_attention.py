@@ -146,3 +146,35 @@ def test_decode_attention_graph_replays():
             g.replay()
             s.synchronize()
             assert torch.equal(out, want), f"replay {i}"
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_decode_attention_full_batch(ties):
+    """The benchmarked shape (batch 64, 32 query heads over 8 KV heads,
+    lengths 256..4096): one split per sequence, workgroups taken in order of
+    length.  With `ties`, most lengths are cut to one value (equal lengths are
+    ordered by index).  Sampled sequences (the longest, the shortest and every
+    eighth) against the oracle; the whole output is deterministic."""
+    d = dev()
+    B, Hq, Hkv = 64, 32, 8
+    note(f"paged decode attention B={B} Hq={Hq} Hkv={Hkv} lengths 256..4096 ties={ties}")
+    inp = synth.attention_inputs(B, Hq, Hkv, 256, 4096, 2400)
+    kc, vc, _, _, _ = _build(inp, Hkv, d)
+    lens = inp["lens"].copy()
+    if ties:
+        lens = np.minimum(lens, 1000).astype(np.int32)
+    q, pages, lt = inp["q"].to(d), torch.from_numpy(inp["pages"]).to(d), torch.from_numpy(lens).to(d)
+    out = sgd.paged_decode_attention(q, kc, vc, inp["n_pages"], pages, lt, Hkv)
+    out2 = sgd.paged_decode_attention(q, kc, vc, inp["n_pages"], pages, lt, Hkv)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "not deterministic"
+    got = out.float().cpu().numpy().astype(np.float64)
+    sample = sorted({int(np.argmax(lens)), int(np.argmin(lens))} | set(range(0, B, 8)))
+    for b in sample:
+        T = int(lens[b])
+        want = att.decode_attention(bf16_to_f64(inp["q"][b:b + 1]), bf16_to_f64(inp["k"][b:b + 1, :T]),
+                                    bf16_to_f64(inp["v"][b:b + 1, :T]), lens[b:b + 1])[0]
+        assert_close(got[b], want, f"decode attention sequence {b} (length {T})")
+        for h in range(Hq):
+            rf = np.linalg.norm(got[b, h] - want[h]) / np.linalg.norm(want[h])
+            assert rf <= 1e-2, (b, h, rf)
