@@ -392,7 +392,9 @@ int sgd_swiglu_mlp_prefill(const uint16_t* x_bf16, int M, const sgd_weight* gate
   if ((rc = launch_act_tiles(fmt, x_bf16, M, d, xq, xs, s))) return rc;
   if ((rc = launch_tile_gemm(fmt, xq, xs, Mpad, d, gate_up, gu, true, s))) return rc;
   if ((rc = launch_swiglu_quantize_tiles(fmt, gu, Mpad, F, aq, as, s))) return rc;
-  return launch_tile_gemm(fmt, aq, as, M, F, down, y_bf16, false, s);
+  // (the second GEMM may split K, its partial sums in the gate/up buffer,
+  // which is no longer read)
+  return launch_tile_gemm(fmt, aq, as, M, F, down, y_bf16, false, s, gu, (size_t)Mpad * 2 * F * 4);
 }
 
 // ---- paged decode attention ----

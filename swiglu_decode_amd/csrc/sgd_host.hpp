@@ -55,7 +55,7 @@ size_t act_tiles_codes_bytes(int M, int K);
 size_t act_tiles_scales_bytes(int fmt, int M, int K);
 int launch_act_tiles(int fmt, const uint16_t* x, int M, int K, uint8_t* codes, void* scales, hipStream_t s);
 int launch_tile_gemm(int fmt, const uint8_t* a, const void* as, int M, int K, const sgd_weight* w, void* c,
-                     bool out_f32, hipStream_t s);
+                     bool out_f32, hipStream_t s, float* part = nullptr, size_t part_bytes = 0);
 // Paged decode attention over an MXFP8 K/V cache (head_dim 128, 16-slot pages).
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int max_pages);
 int launch_kv_write(int kind, const uint16_t* x, const int32_t* slots, int n, int Hkv, uint8_t* cache, int n_pages,

@@ -35,6 +35,7 @@ namespace sgd {
 namespace {
 
 constexpr uint32_t OOB_T = 0x80000000u;  // a buffer offset past every buffer's end
+constexpr int KSPLIT_CUS = 256;          // compute units a split-K launch aims to fill
 
 struct TileArgs {
   const uint8_t* a;  // Q(x) codes, full m-tiles [Mpad/16][K/128][2048]
@@ -46,7 +47,8 @@ struct TileArgs {
   void* c;           // [M, N] bf16 or fp32 (row-major)
   int M;             // rows of C stored
   uint32_t a_bytes, as_bytes, w_bytes, ws_bytes;
-  int tiles_m;       // blocks along M (the grid is tiles_m x blocks along N)
+  int tiles_m;       // blocks along M (the grid is tiles_m x blocks along N, times ksplit)
+  int ksplit;        // K ranges: range r writes fp32 partial sums at c + r*M*N (OUT 1), summed by a second kernel
 };
 
 __device__ __forceinline__ int uni_t(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -78,8 +80,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
   const uint32_t trash = lds0 + (uint32_t)(NSTG * SB);
   const int l = lane_id(), wv = uni_t((int)(threadIdx.x >> 6));
   const int wm = wv % WGM, wn = wv / WGM;
-  const int bm = blockIdx.x % p.tiles_m, bn = blockIdx.x / p.tiles_m;
-  const int KT = p.K >> 7;
+  const int nblk = (int)gridDim.x / p.ksplit;
+  const int kr = (int)blockIdx.x / nblk, blk = (int)blockIdx.x - kr * nblk;
+  const int bm = blk % p.tiles_m, bn = blk / p.tiles_m;
+  const int KTall = p.K >> 7;
+  // this block's k-tiles [k0, KT)
+  const int k0 = (int)(((long long)kr * KTall) / p.ksplit), KT = (int)(((long long)(kr + 1) * KTall) / p.ksplit);
   const int mt0 = bm * AT, nb0 = bn * BT;  // first m-tile / n-block of the block
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes), rw = make_rsrc(p.w, p.w_bytes);
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(p.as, p.as_bytes), rws = make_rsrc(p.ws, p.ws_bytes);
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
         lds_copy1k(ra, m0, in && mt < MTA ? (uint32_t)mt * 16u * (uint32_t)p.K + ukt * 2048u + lo : OOB_T);
       } else {
         const int nb = nb0 + t - AT;
-        lds_copy1k(rw, m0, in && nb < NBW ? ((uint32_t)nb * (uint32_t)KT + ukt) * 2048u + lo : OOB_T);
+        lds_copy1k(rw, m0, in && nb < NBW ? ((uint32_t)nb * (uint32_t)KTall + ukt) * 2048u + lo : OOB_T);
       }
     }
     const uint32_t sbase = base + (uint32_t)((AT + BT) * 2048);
@@ -123,14 +129,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
         const uint32_t dst = sbase + (uint32_t)(AT * 64 + (c - AT / 4) * 256);
         if (FMT == FMT_MX) {
           const int nb = nb0 + c - AT / 4;
-          const uint32_t KG = (uint32_t)(KT + 3) >> 2;
+          const uint32_t KG = (uint32_t)(KTall + 3) >> 2;
           const uint32_t o = ((uint32_t)nb * KG + (ukt >> 2)) * 256u + (uint32_t)l * 4u;
           lds_copy256(rws, dst, in && nb < NBW ? o : OOB_T);
         } else {
           // lane j: the scale of the workgroup's j-th 128-row weight block
-          const int blk = (nb0 >> 3) + l;
-          const bool ok = in && l < BT / 8 && blk * 8 < NBW;
-          lds_copy256(rws, dst, ok ? ((uint32_t)blk * (uint32_t)KT + ukt) * 4u : OOB_T);
+          const int wblk = (nb0 >> 3) + l;
+          const bool ok = in && l < BT / 8 && wblk * 8 < NBW;
+          lds_copy256(rws, dst, ok ? ((uint32_t)wblk * (uint32_t)KTall + ukt) * 4u : OOB_T);
         }
       } else {
         lds_copy256(ras, trash, OOB_T);
@@ -148,12 +154,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
   // per k-tile both publishes stage kt (every wavefront has waited for its
   // own copies of it) and frees stage kt - 1 for the copy of kt + NSTG - 1
 #pragma unroll
-  for (int b = 0; b < NSTG - 1; ++b) copy_stage(b, b);
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int b = 0; b < NSTG - 1; ++b) copy_stage(k0 + b, b);
+  for (int kt = k0; kt < KT; ++kt) {
+    const int j0 = kt - k0;  // (stage index: the range's own position)
     lds_copies_left<(NSTG - 2) * OPS>();
     __syncthreads();
-    copy_stage(kt + NSTG - 1, (kt + NSTG - 1) % NSTG);
-    const uint8_t* st = lds + (kt % NSTG) * SB;
+    copy_stage(kt + NSTG - 1, (j0 + NSTG - 1) % NSTG);
+    const uint8_t* st = lds + (j0 % NSTG) * SB;
     const uint8_t* ssa = st + (AT + BT) * 2048;
     const uint8_t* ssb = ssa + AT * 64;
     v8i av[TM];
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tile_gemm_kernel(TileArgs p) {
         if (row < p.M && col < p.N) {
           const size_t o = (size_t)row * p.N + col;
           if (OUT == 1)
-            static_cast<float*>(p.c)[o] = acc[i][j][rr];
+            static_cast<float*>(p.c)[(size_t)kr * p.M * p.N + o] = acc[i][j][rr];
           else
             static_cast<uint16_t*>(p.c)[o] = (uint16_t)f32_to_bf16(acc[i][j][rr]);
         }
@@ -257,13 +264,31 @@ __global__ __launch_bounds__(256) void act_tiles_kernel(const uint16_t* __restri
   }
 }
 
+// y [M, N] bf16 = the sum of the S fp32 partials [S][M][N] (in range order),
+// four elements per lane.
+__global__ __launch_bounds__(256) void ksum_kernel(const float* __restrict__ part, int S, long long n,
+                                                   uint16_t* __restrict__ y) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 v = *reinterpret_cast<const float4*>(part + i);
+  for (int r = 1; r < S; ++r) {
+    const float4 w = *reinterpret_cast<const float4*>(part + (size_t)r * n + i);
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  const uint32_t lo = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), hi = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
+  *reinterpret_cast<uint2*>(y + i) = make_uint2(lo, hi);
+}
+
 template <int FMT, int WGM, int WGN, int TM, int TN, int NSTG, int OUT>
 int launch_tile_cfg(TileArgs p, hipStream_t s) {
   constexpr int BM = WGM * TM * 16, BN = WGN * TN * 16;
   constexpr size_t lds = (size_t)NSTG * tile_stage_bytes<WGM * TM, WGN * TN>() + TRASH_BYTES;
   static_assert(lds <= 163840, "LDS of one workgroup");
   p.tiles_m = (p.Mpad + BM - 1) / BM;
-  const long long grid = (long long)p.tiles_m * ((p.N + BN - 1) / BN);
+  const long long grid = (long long)p.tiles_m * ((p.N + BN - 1) / BN) * p.ksplit;
   auto k = tile_gemm_kernel<FMT, WGM, WGN, TM, TN, NSTG, OUT>;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
       hipSuccess)
@@ -298,9 +323,13 @@ int launch_act_tiles(int fmt, const uint16_t* x, int M, int K, uint8_t* codes, v
 }
 
 // C [M, N] (bf16, or fp32 when out_f32) = Q(A) W^T for Q(A) in the full-tile
-// workspace layout of Mpad >= M rows.
+// workspace layout of Mpad >= M rows.  With `part` (fp32, part_bytes) and a
+// bf16 C that the 128 x 128 blocks alone would spread over fewer workgroups
+// than compute units: K is split into S ranges (S blocks per compute unit
+// at most, at least 16 k-tiles each), whose fp32 partial sums go to `part`
+// and are added by a second kernel.
 int launch_tile_gemm(int fmt, const uint8_t* a, const void* as, int M, int K, const sgd_weight* w, void* c,
-                     bool out_f32, hipStream_t s) {
+                     bool out_f32, hipStream_t s, float* part, size_t part_bytes) {
   TileArgs p{};
   p.a = a;
   p.as = as;
@@ -318,6 +347,24 @@ int launch_tile_gemm(int fmt, const uint8_t* a, const void* as, int M, int K, co
   // the big blocks when they still give at least one per compute unit
   const long long big_blocks = (long long)((p.Mpad + 255) / 256) * ((p.N + 127) / 128);
   const bool big = big_blocks >= 256;
+  p.ksplit = 1;
+  if (!big && !out_f32 && part) {
+    const long long blocks = (long long)((p.Mpad + 127) / 128) * ((p.N + 127) / 128);
+    int S = (int)(KSPLIT_CUS / blocks);
+    if (S > (K / 128) / 16) S = (K / 128) / 16;
+    while (S > 1 && (size_t)S * (size_t)M * (size_t)p.N * 4u > part_bytes) --S;
+    if (S > 1) {
+      p.ksplit = S;
+      p.c = part;
+      const int rc = fmt == FMT_BLOCK ? launch_tile_gemm_fmt<FMT_BLOCK, 1>(p, false, s)
+                                      : launch_tile_gemm_fmt<FMT_MX, 1>(p, false, s);
+      if (rc) return rc;
+      const long long n = (long long)M * p.N;  // (a multiple of 4: N is of 128)
+      hipLaunchKernelGGL(ksum_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, S, n,
+                         static_cast<uint16_t*>(c));
+      return hip_status(hipGetLastError());
+    }
+  }
   if (fmt == FMT_BLOCK)
     return out_f32 ? launch_tile_gemm_fmt<FMT_BLOCK, 1>(p, big, s) : launch_tile_gemm_fmt<FMT_BLOCK, 0>(p, big, s);
   return out_f32 ? launch_tile_gemm_fmt<FMT_MX, 1>(p, big, s) : launch_tile_gemm_fmt<FMT_MX, 0>(p, big, s);
