@@ -55,7 +55,10 @@ def test_kv_cache_write_bit_exact():
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,lo,hi", [(5, 8, 2, 1, 200), (3, 16, 1, 1, 40), (4, 4, 4, 15, 17),
-                                            (8, 32, 8, 1, 2000), (2, 32, 8, 3000, 5000)])
+                                            (8, 32, 8, 1, 2000), (2, 32, 8, 3000, 5000),
+                                            # one split each: the largest batch taken in order of
+                                            # length, and one past it (dispatch order)
+                                            (256, 4, 2, 1, 100), (300, 8, 2, 1, 64)])
 def test_decode_attention_parity(B, Hq, Hkv, lo, hi):
     d = dev()
     note(f"paged decode attention B={B} Hq={Hq} Hkv={Hkv} lengths {lo}..{hi}")
