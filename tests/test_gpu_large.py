@@ -120,6 +120,25 @@ def test_mlp_prefill_parity(name, fmt, M):
         print(f"[report] prefill vs fused {name} {fmt} M={M}: rel_fro={rf:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("fmt", ["block", "mx"])
+def test_mlp_prefill_uneven_ksplit(fmt):
+    """d=1024, ffn=4480 (35 k-tiles), M=100: the down projection's 8 blocks
+    split K in two ranges of 17 and 18 k-tiles, the second starting inside a
+    group of four MX scale k-tiles; the fp32 partials summed by the second
+    kernel.  Against the oracle."""
+    d = dev()
+    note(f"prefill MLP d=1024 ffn=4480 {fmt} M=100 (split K)")
+    wl = synth.Workload("ksplit", 1024, 4480, (100,), (fmt,), 1011)
+    inp = synth.mlp_inputs(wl)
+    M = 100
+    x = inp["x"][:M]
+    pg, pu, pd = [sgd.quantize_pack_weight(inp[k].to(d), fmt) for k in ("wg", "wu", "wd")]
+    y = sgd.swiglu_mlp_prefill(x.to(d), sgd.stack_packed(pg, pu), pd)
+    torch.cuda.synchronize()
+    q = [oracle_weight(inp[k], fmt) for k in ("wg", "wu", "wd")]
+    assert_close(gpu_out_f64(y), ref.swiglu_mlp(bf16_to_f64(x), *q), f"prefill MLP split K {fmt}")
+
+
 def test_mlp_prefill_d4096_m1024_sampled_rows():
     """d=4096, ffn=12288 MXFP8 at M=1024: 24 sampled rows against the oracle
     (rows of the MLP are independent)."""
