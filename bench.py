@@ -560,7 +560,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the MLP would shard over ffn with one all-reduce of y; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
